@@ -1,0 +1,223 @@
+"""numpy float64 oracle of one canvas denoise step (and the causal append).
+
+Each function follows a passage of the DiffusionGemma explainer; readings of
+what the pages leave open are stated where they are used.  Shapes:
+
+  H      [B, C, d]        canvas hidden states (the backbone's input rows)
+  E      [V, d]           token-embedding table, also the (tied) vocabulary head
+  Wq     [Hq*dh, d]       projection weights stored output-major (linear layer)
+  Wk, Wv [Hkv*dh, d]
+  Wo     [d, Hq*dh]
+  Kc, Vc [B, Hkv, cap, dh] KV cache, rows [0, L) valid
+  x      [B, C] int       canvas tokens
+  S      [B, C, d]        self-conditioning vector from the previous step
+
+All float inputs are float64 arrays holding the stored (already rounded)
+values; ``dtype`` names the storage precision that API-visible results are
+rounded to.
+"""
+import math
+
+import numpy as np
+
+from .numerics import round_store
+from .philox import draw_tokens
+
+
+# -- assemble -------------------------------------------------------------------
+
+def assemble(H, E, x, S_prev, dtype):
+    """The denoiser reads the canvas (its tokens' embeddings) on top of the
+    hidden rows, plus the self-conditioning vector handed over from the
+    previous step ("Autocondizionamento": the result is passed directly to the
+    next step).  Reading taken: X = H + E[x] + S_prev with S_prev = 0 on a
+    block's first step; no embedding scale."""
+    X = H + E[x]
+    if S_prev is not None:
+        X = X + S_prev
+    return round_store(X, dtype)
+
+
+def linear(X, W, dtype):
+    """Y = X . W^T for an output-major weight W[out, in]; stored rounding."""
+    return round_store(X @ W.T, dtype)
+
+
+# -- attention --------------------------------------------------------------------
+
+def attention(Q, Kc, Vc, Kn, Vn, L, causal, dtype=None):
+    """Canvas attention over [cache rows 0..L) || canvas rows 0..C).
+
+    Denoise mode ("Architettura...", bidirectional denoising): every canvas
+    query attends to every canvas token and to the whole KV cache -- no mask.
+    Prefill mode (same section, causal prefill): query i sees the whole cache
+    and canvas keys 0..i, i.e. key j is kept iff j < L + i + 1.
+
+    GQA: query head h uses KV head floor(h / (Hq/Hkv)).  Scores are scaled by
+    1/sqrt(dh) (reading: the standard scale; the pages give none).
+    Returns O [B, C, Hq, dh] (rounded to dtype when given) and the natural-log
+    sum-exp of the scaled scores, lse [B, C, Hq] (float64).
+    """
+    B, C, Hq, dh = Q.shape
+    Hkv = Kn.shape[2]
+    G = Hq // Hkv
+    O = np.empty((B, C, Hq, dh))
+    lse = np.empty((B, C, Hq))
+    scale = 1.0 / math.sqrt(dh)
+    if causal:
+        j = np.arange(L + C)[None, :]
+        i = np.arange(C)[:, None]
+        keep = j < (L + i + 1)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            keys = np.concatenate([Kc[b, g, :L], Kn[b, :, g]], axis=0)   # [L+C, dh]
+            vals = np.concatenate([Vc[b, g, :L], Vn[b, :, g]], axis=0)
+            s = (Q[b, :, h] @ keys.T) * scale                              # [C, L+C]
+            if causal:
+                s = np.where(keep, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            l = p.sum(axis=1, keepdims=True)
+            O[b, :, h] = (p @ vals) / l
+            lse[b, :, h] = (m + np.log(l))[:, 0]
+    if dtype is not None:
+        O = round_store(O, dtype)
+    return O, lse
+
+
+# -- vocabulary head, confidence and self-conditioning ----------------------------
+
+def vocab_selfcond(Z, E, dtype=None, chunk=16384):
+    """Full-vocabulary softmax of the tied head l = Z . E^T, per row:
+
+      m   = max_v l_v                  a = lowest v attaining m
+      lse = m + ln sum_v exp(l_v - m)  c = exp(m - lse)  (max probability)
+      S   = sum_v P_v E_v with P = exp(l - lse)
+
+    Confidence is the largest probability of the row (reading of "se la
+    probabilita di un token scende al di sotto di una soglia", "Diffusione
+    dello stato uniforme": the confidence of the position's prediction).
+    S is the probability matrix times the embedding table
+    ("Autocondizionamento").  Two plain passes over the vocabulary in chunks:
+    the first finds m and a, the second sums exp(l - m) and exp(l - m) E_v.
+    Z [R, d], E [V, d] -> m, a, lse, c [R] and S [R, d] (rounded to dtype when
+    given).
+    """
+    R = Z.shape[0]
+    V = E.shape[0]
+    m = np.full(R, -np.inf)
+    a = np.zeros(R, np.int64)
+    for v0 in range(0, V, chunk):
+        lg = Z @ E[v0:v0 + chunk].T
+        cm = lg.max(axis=1)
+        ca = lg.argmax(axis=1) + v0          # first index among equal maxima
+        better = cm > m                      # earlier chunk wins a tie
+        a = np.where(better, ca, a)
+        m = np.where(better, cm, m)
+    l = np.zeros(R)
+    St = np.zeros((R, E.shape[1]))
+    for v0 in range(0, V, chunk):
+        Ec = E[v0:v0 + chunk]
+        p = np.exp(Z @ Ec.T - m[:, None])
+        l += p.sum(axis=1)
+        St += p @ Ec
+    lse = m + np.log(l)
+    c = np.exp(m - lse)
+    S = St / l[:, None]
+    if dtype is not None:
+        S = round_store(S, dtype)
+    return m, a, lse, c, S
+
+
+def vocab_rows(Z_rows, E):
+    """The same quantities for a few rows, computed from the full logits row at
+    once (used for sampled parity at full vocabulary size)."""
+    lg = Z_rows @ E.T
+    m = lg.max(axis=1)
+    a = lg.argmax(axis=1)
+    p = np.exp(lg - m[:, None])
+    l = p.sum(axis=1)
+    srt = np.sort(lg, axis=1)
+    gap = srt[:, -1] - srt[:, -2]
+    return m, a, m + np.log(l), 1.0 / l, (p @ E) / l[:, None], gap
+
+
+# -- uniform-state renoise ---------------------------------------------------------
+
+def renoise(a, c, tau, seed, t, block, B, C, V):
+    """"Diffusione dello stato uniforme": a position whose probability drops
+    below the threshold is renoised with a new random vocabulary token; the
+    others keep the model's prediction.  Readings: the probability is the
+    confidence c (max probability); "below" is strict (c < tau, the threshold
+    taken as a float32 as the kernel receives it); a kept position takes the
+    argmax a; the replacement is uniform over all V ids (Philox draw t).
+    a, c: [B*C] -> new tokens [B*C] int64, mask [B*C] uint8."""
+    tau32 = float(np.float32(tau))
+    mask = (np.asarray(c, np.float64) < tau32)
+    U = draw_tokens(seed, t, block, B, C, V).reshape(-1)
+    x_new = np.where(mask, U, np.asarray(a, np.int64))
+    return x_new, mask.astype(np.uint8)
+
+
+def init_canvas(seed, block, B, C, V):
+    """A block's canvas starts as random vocabulary tokens ("Il problema con i
+    modelli autoregressivi": 256 random tokens; table row "Punto iniziale").
+    Draw index t = 0."""
+    return draw_tokens(seed, 0, block, B, C, V)
+
+
+# -- the step -------------------------------------------------------------------
+
+def denoise_step(H, E, W, Kc, Vc, L, x, S_prev, tau, seed, t, block, dtype):
+    """One denoise step over all B canvases.  W = dict(Wq, Wk, Wv, Wo).
+
+    1 X = H + E[x] + S_prev                  (assemble)
+    2 Q, K_new, V_new = X Wq^T, X Wk^T, X Wv^T
+    3 O = bidirectional attention over [cache || canvas]
+    4 Z = X + O Wo^T                          (residual)
+    5 m, a, lse, c, S = vocab head and self-conditioning of Z
+    6 x', mask = renoise(a, c)                (draw index t)
+    The cache is only read (denoise never writes it; only prefill does,
+    "Architettura...").  Returns a dict of every intermediate.
+    """
+    B, C, d = H.shape
+    dh = Kc.shape[3]
+    Hq = W["Wq"].shape[0] // dh
+    Hkv = W["Wk"].shape[0] // dh
+    V = E.shape[0]
+    X = assemble(H, E, x, S_prev, dtype)
+    Xf = X.reshape(B * C, d)
+    Q = linear(Xf, W["Wq"], dtype).reshape(B, C, Hq, dh)
+    Kn = linear(Xf, W["Wk"], dtype).reshape(B, C, Hkv, dh)
+    Vn = linear(Xf, W["Wv"], dtype).reshape(B, C, Hkv, dh)
+    O, lse_att = attention(Q, Kc, Vc, Kn, Vn, L, causal=False, dtype=dtype)
+    Z = round_store(Xf + O.reshape(B * C, Hq * dh) @ W["Wo"].T, dtype)
+    m, a, lse, c, S = vocab_selfcond(Z, E, dtype)
+    x_new, mask = renoise(a, c, tau, seed, t, block, B, C, V)
+    return dict(X=X, Q=Q, Kn=Kn, Vn=Vn, O=O, lse_att=lse_att, Z=Z.reshape(B, C, d),
+                m=m, a=a, lse=lse, c=c, S=S.reshape(B, C, d),
+                x_new=x_new.reshape(B, C), mask=mask.reshape(B, C))
+
+
+def prefill_append(H, E, W, Kc, Vc, L, x_final, dtype):
+    """Incremental prefill of a finished block ("Architettura...": causal
+    attention writes the KV cache, once per block, before the next canvas;
+    "Campionamento multi-canvas": the completed block joins the context).
+    X = H + E[x_final] (no self-conditioning), K_new/V_new written at cache
+    rows [L, L+C), then causal attention (query i sees the cache and canvas
+    keys 0..i).  Returns (Kc', Vc', O, lse) with copies of the caches."""
+    B, C, d = H.shape
+    dh = Kc.shape[3]
+    Hq = W["Wq"].shape[0] // dh
+    Hkv = W["Wk"].shape[0] // dh
+    X = assemble(H, E, x_final, None, dtype).reshape(B * C, d)
+    Q = linear(X, W["Wq"], dtype).reshape(B, C, Hq, dh)
+    Kn = linear(X, W["Wk"], dtype).reshape(B, C, Hkv, dh)
+    Vn = linear(X, W["Wv"], dtype).reshape(B, C, Hkv, dh)
+    O, lse = attention(Q, Kc, Vc, Kn, Vn, L, causal=True, dtype=dtype)
+    Kc2 = Kc.copy()
+    Vc2 = Vc.copy()
+    Kc2[:, :, L:L + C] = Kn.transpose(0, 2, 1, 3)
+    Vc2[:, :, L:L + C] = Vn.transpose(0, 2, 1, 3)
+    return Kc2, Vc2, O, lse
