@@ -1,0 +1,171 @@
+/*
+ * dg.h -- C ABI of the canvas denoise step for uniform-state text diffusion,
+ * hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one the DiffusionGemma explainer describes
+ * (ai.google.dev, "DiffusionGemma explained"; sections cited by their Italian
+ * headings).  One denoise step over a canvas of C tokens:
+ *
+ *   X   = H + E[x] + S_prev                     self-conditioning input
+ *   Q,K,V = X Wq^T, X Wk^T, X Wv^T              projections
+ *   O   = attention(Q; [cache || canvas])       bidirectional, no mask
+ *   Z   = X + O Wo^T
+ *   l   = Z E^T;  m = max l;  a = argmax l;  c = exp(m - lse)
+ *   S   = softmax(l) E                          P.E, P never stored
+ *   x'  = c < tau ? uniform token : a           uniform-state renoise
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *    library never allocates, frees, copies to the host or synchronises.
+ *    Every call only enqueues kernels on `stream` (a hipStream_t; NULL is the
+ *    default stream), so calls can be captured in a HIP graph.
+ *  - Tensors are dense row-major in the index order written next to them.
+ *    Floating tensors are float32 (DG_F32) or bfloat16 bit patterns
+ *    (DG_BF16) as selected by `dtype`; statistics (max_logit, conf, lse) are
+ *    always float32, token ids int32, masks uint8.  bf16 inputs are multiplied
+ *    exactly and accumulated in float32; bf16 outputs are rounded to nearest
+ *    even.
+ *  - Base pointers of bf16 tensors must be 16-byte aligned.
+ *  - Outputs must not alias inputs except where an entry point says so.
+ *  - Arguments are checked before anything is enqueued: a failed check returns
+ *    a negative dg_status, enqueues nothing and leaves outputs untouched; the
+ *    reason is in dg_last_error() (per calling thread).  A HIP launch failure
+ *    returns DG_EHIP.  Nothing aborts, prints or throws across the ABI.
+ *  - Token ids read by a kernel must lie in [0, V); an id outside that range
+ *    is read as id 0 (never out of bounds).
+ *  - The library is stateless and reentrant; concurrent calls on different
+ *    streams must use different workspaces.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+
+typedef enum {
+  DG_OK = 0,
+  DG_EINVAL = -1,        /* NULL pointer, bad size, bad alignment, Hq % Hkv != 0 ... */
+  DG_EUNSUPPORTED = -2,  /* valid but not implemented (e.g. bf16 head_dim not 64/128) */
+  DG_EWORKSPACE = -3,    /* workspace NULL or smaller than the *_workspace_bytes figure */
+  DG_EHIP = -4           /* a HIP call failed; text in dg_last_error() */
+} dg_status;
+
+/* Sizes of one step.  B canvases of C tokens; the cache holds `cap` rows per
+ * (canvas, KV head), of which rows [0, L) are valid.  GQA: query head h reads
+ * KV head h / (n_q_heads / n_kv_heads). */
+typedef struct {
+  int32_t B, C, L, cap, d, n_q_heads, n_kv_heads, head_dim, V;
+  int32_t dtype; /* dg_dtype */
+} dg_dims;
+
+/* Model tensors.  Projection weights are stored output-major, like a linear
+ * layer's weight: Wq[Hq*dh][d], Wk[Hkv*dh][d], Wv[Hkv*dh][d], Wo[d][Hq*dh].
+ * E[V][d] is the token-embedding table, also the tied vocabulary head. */
+typedef struct {
+  const void *Wq, *Wk, *Wv, *Wo, *E;
+} dg_weights;
+
+/* Per-step tensors (R = B*C rows, row r = canvas r / C, position r % C). */
+typedef struct {
+  const void *H;            /* [B][C][d] canvas hidden rows */
+  const void *k_cache;      /* [B][Hkv][cap][dh]; rows [0, L) are read */
+  const void *v_cache;      /* [B][Hkv][cap][dh] */
+  const int32_t *tokens_in; /* [B][C] canvas tokens x_t */
+  const void *selfcond_in;  /* [B][C][d] S from the previous step; NULL reads 0 */
+  int32_t *tokens_out;      /* [B][C] x_{t+1}; may equal tokens_in */
+  void *selfcond_out;       /* [B][C][d] S of this step; may equal selfcond_in */
+  float *max_logit;         /* [R] m */
+  float *conf;              /* [R] c = max probability */
+  float *lse;               /* [R] log-sum-exp of the logits; may be NULL */
+  int32_t *argmax;          /* [R] lowest id attaining m */
+  uint8_t *mask;            /* [R] 1 where the position was renoised; may be NULL */
+  /* Optional copies of the intermediates (NULL: kept in the workspace). */
+  void *x_out;              /* [R][d]        X */
+  void *q_out;              /* [R][Hq][dh]   Q */
+  void *k_new_out;          /* [R][Hkv][dh]  canvas keys */
+  void *v_new_out;          /* [R][Hkv][dh]  canvas values */
+  void *attn_out;           /* [R][Hq][dh]   O */
+  void *z_out;              /* [R][d]        Z */
+} dg_step_io;
+
+/* Workspace bytes needed by dg_denoise_step and dg_prefill_append for dims. */
+size_t dg_workspace_bytes(const dg_dims *dims);
+
+/* One denoise step for all B canvases ("Diffusione dello stato uniforme" and
+ * "Autocondizionamento"; attention as in "Architettura: il prefill
+ * incrementale e il denoising", denoising mode).  The cache is only read.
+ * tau: renoise threshold (a position is renoised iff conf < tau).
+ * seed, t, block: Philox4x64-10 key (seed, 0) and counter words (position i,
+ * draw index t, canvas b, block); the initial canvas of a block is draw 0,
+ * so denoise step s of a block should pass t = s + 1.
+ * ws/ws_bytes: device workspace of at least dg_workspace_bytes(dims). */
+int dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_step_io *io,
+                    float tau, uint64_t seed, uint32_t t, uint32_t block,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* Canvas attention ("Architettura..."): for canvas b, query head h, position
+ * i, O = softmax_j(q.k_j / sqrt(dh)) v_j over keys j in
+ * [k_cache[b][g][0..L) || k_new[b][0..C)[g]], g = h / (Hq/Hkv).
+ * causal = 0: every key (denoising).  causal = 1: key j is kept iff
+ * j < L + i + 1 (prefill of a block after an L-row cache).
+ * q[B][C][Hq][dh], k_new/v_new[B][C][Hkv][dh], caches as in dg_step_io,
+ * out[B][C][Hq][dh]; lse_out[B][C][Hq] (natural log, float32) may be NULL.
+ * Only dims->{B,C,L,cap,n_q_heads,n_kv_heads,head_dim,dtype} are used. */
+size_t dg_attn_workspace_bytes(const dg_dims *dims);
+int dg_attn_bidir(const dg_dims *dims, const void *q, const void *k_cache, const void *v_cache,
+                  const void *k_new, const void *v_new, void *out, float *lse_out, int causal,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* Vocabulary head, confidence and self-conditioning ("Autocondizionamento";
+ * confidence as in "Diffusione dello stato uniforme"): for each of `rows`
+ * rows of z[rows][d] and E[V][d]: logits l = z E^T,
+ * max_logit = max l, argmax = lowest id attaining it, lse = log sum exp l,
+ * conf = exp(max_logit - lse), selfcond[rows][d] = softmax(l) E.
+ * The rows x V probability matrix is never stored.  lse may be NULL. */
+size_t dg_vocab_workspace_bytes(int32_t rows, int32_t d, int32_t V, int32_t dtype);
+int dg_vocab_selfcond(int32_t rows, int32_t d, int32_t V, int32_t dtype, const void *z,
+                      const void *E, float *max_logit, int32_t *argmax, float *conf, float *lse,
+                      void *selfcond, void *ws, size_t ws_bytes, void *stream);
+
+/* Uniform-state renoise ("Diffusione dello stato uniforme"): row r (canvas
+ * b = r / canvas, position i = r % canvas) becomes
+ *   conf[r] < tau ? floor(w0 * V / 2^64) : argmax[r],
+ * w0 = word 0 of Philox4x64-10(counter (i, t, b, block), key (seed, 0)).
+ * mask_out[r] = 1 where a token was drawn (may be NULL).  tokens_out may
+ * equal argmax. */
+int dg_renoise(int32_t rows, int32_t canvas, int32_t V, const int32_t *argmax, const float *conf,
+               float tau, uint64_t seed, uint32_t t, uint32_t block, int32_t *tokens_out,
+               uint8_t *mask_out, void *stream);
+
+/* A block's starting canvas ("Il problema con i modelli autoregressivi":
+ * random vocabulary tokens): every row drawn as in dg_renoise with t = 0. */
+int dg_init_canvas(int32_t rows, int32_t canvas, int32_t V, uint64_t seed, uint32_t block,
+                   int32_t *tokens_out, void *stream);
+
+/* Incremental prefill of a finished block ("Architettura...", causal
+ * prefill; "Campionamento multi-canvas (diffusione a blocchi)"):
+ * X = H + E[tokens_final] (no self-conditioning), canvas keys/values
+ * X Wk^T, X Wv^T are written to cache rows [L, L+C) of every (canvas, KV
+ * head), and causal attention of X Wq^T over [cache rows 0..L) || canvas] is
+ * written to attn_out[B][C][Hq][dh] (may be NULL: then it goes to the
+ * workspace).  Requires L + C <= cap.  The caller then uses L + C as the
+ * cache length. */
+int dg_prefill_append(const dg_dims *dims, const dg_weights *w, const void *H,
+                      const int32_t *tokens_final, void *k_cache, void *v_cache, void *attn_out,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Text of a dg_status; text of the last failure on the calling thread. */
+const char *dg_status_str(int status);
+const char *dg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

@@ -86,6 +86,22 @@ def attention(Q, Kc, Vc, Kn, Vn, L, causal, dtype=None):
     return O, lse
 
 
+def attention_row(q, b, g, i, Kc, Vc, Kn, Vn, L, causal):
+    """The same attention for one query vector q [dh] of canvas b at position
+    i, read against KV head g (used to check sampled rows at full size).
+    Returns (o [dh], lse)."""
+    keys = np.concatenate([Kc[b, g, :L], Kn[b, :, g]], axis=0)
+    vals = np.concatenate([Vc[b, g, :L], Vn[b, :, g]], axis=0)
+    if causal:
+        keys = keys[:L + i + 1]
+        vals = vals[:L + i + 1]
+    s = (keys @ q) / math.sqrt(q.shape[0])
+    m = s.max()
+    p = np.exp(s - m)
+    l = p.sum()
+    return (p @ vals) / l, m + math.log(l)
+
+
 # -- vocabulary head, confidence and self-conditioning ----------------------------
 
 def vocab_selfcond(Z, E, dtype=None, chunk=16384):

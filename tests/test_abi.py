@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports every entry point include/dg.h declares,
+and rejects bad arguments before anything touches the GPU (these calls return
+from the argument checks, so they run on a machine without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import uniform_state_discrete_amd as dg
+    if not os.path.exists(dg.LIB_PATH):
+        from uniform_state_discrete_amd import build
+        build.build()
+    return dg
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("dg_denoise_step", "dg_attn_bidir", "dg_vocab_selfcond", "dg_renoise",
+              "dg_prefill_append", "dg_init_canvas", "dg_workspace_bytes", "dg_status_str",
+              "dg_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    raw = ctypes.CDLL(L.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(raw, n)]
+    assert not missing, missing
+
+
+def test_status_strings(L):
+    lib = L.lib()
+    for code in (0, -1, -2, -3, -4):
+        assert lib.dg_status_str(code).decode().startswith("DG_")
+    assert b"unknown" in lib.dg_status_str(7)
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails its argument checks
+
+
+def dims(**kw):
+    import uniform_state_discrete_amd as dg
+    base = dict(B=1, C=256, L=1024, cap=1024, d=2048, n_q_heads=16, n_kv_heads=8, head_dim=128,
+                V=32768, dtype=dg.DG_BF16)
+    base.update(kw)
+    return dg.make_dims(**base)
+
+
+def test_workspace_sizes(L):
+    from synth import CONFIGS
+    for c in CONFIGS:
+        d = L.make_dims(c.B, c.C, c.L, c.cap, c.d, c.Hq, c.Hkv, c.dh, c.V,
+                        L.DG_BF16 if c.dtype == "bf16" else L.DG_F32)
+        assert L.dg_workspace_bytes(d) > 0, c.name
+    assert L.dg_workspace_bytes(dims(n_kv_heads=7)) == 0
+    assert L.dg_vocab_workspace_bytes(256, 2048, 262144, L.DG_BF16) > 256 * 2048 * 4
+    assert L.dg_vocab_workspace_bytes(16, 64, 512, L.DG_F32) == 0
+
+
+def _step(L, d, ws_bytes=1 << 40, null=(), weights_null=(), ws=FAKE):
+    lib = L.lib()
+    w = L.Weights(*[None if k in weights_null else FAKE for k in ("Wq", "Wk", "Wv", "Wo", "E")])
+    io = L.StepIO(*[None if (k in null or k in ("selfcond_in", "lse", "mask", "x_out", "q_out",
+                                                 "k_new_out", "v_new_out", "attn_out", "z_out"))
+                    else FAKE for k in L.STEP_IO_FIELDS])
+    return lib.dg_denoise_step(ctypes.byref(d), ctypes.byref(w), ctypes.byref(io), 0.9, 1, 1, 0,
+                               ws, ws_bytes, None)
+
+
+def test_step_argument_checks(L):
+    lib = L.lib()
+    assert _step(L, dims(), null=("H",)) == L.DG_EINVAL
+    assert _step(L, dims(), weights_null=("E",)) == L.DG_EINVAL
+    assert _step(L, dims(n_kv_heads=3)) == L.DG_EINVAL
+    assert _step(L, dims(B=0)) == L.DG_EINVAL
+    assert _step(L, dims(L=2000, cap=1024)) == L.DG_EINVAL
+    assert _step(L, dims(dtype=5)) == L.DG_EINVAL
+    assert _step(L, dims(head_dim=96)) == L.DG_EUNSUPPORTED
+    assert _step(L, dims(d=1000)) == L.DG_EUNSUPPORTED
+    assert _step(L, dims(), ws_bytes=1000) == L.DG_EWORKSPACE
+    assert _step(L, dims(), ws=None) == L.DG_EWORKSPACE
+    assert b"workspace" in lib.dg_last_error()
+    # misaligned bf16 tensor
+    w = L.Weights(FAKE, FAKE + 2, FAKE, FAKE, FAKE)
+    io = L.StepIO(*[FAKE if k in ("H", "k_cache", "v_cache", "tokens_in", "tokens_out", "selfcond_out",
+                                  "max_logit", "conf", "argmax") else None for k in L.STEP_IO_FIELDS])
+    st = lib.dg_denoise_step(ctypes.byref(dims()), ctypes.byref(w), ctypes.byref(io), 0.9, 1, 1, 0,
+                             FAKE, 1 << 40, None)
+    assert st == L.DG_EINVAL and b"aligned" in lib.dg_last_error()
+
+
+def test_component_argument_checks(L):
+    lib = L.lib()
+    vp = ctypes.c_void_p
+    # vocab
+    assert lib.dg_vocab_selfcond(0, 2048, 100, L.DG_BF16, *[vp(FAKE)] * 7, vp(FAKE), 1 << 40, None) == L.DG_EINVAL
+    assert lib.dg_vocab_selfcond(4, 2048, 100, L.DG_BF16, None, *[vp(FAKE)] * 6, vp(FAKE), 1 << 40, None) == L.DG_EINVAL
+    assert lib.dg_vocab_selfcond(4, 3000, 100, L.DG_BF16, *[vp(FAKE)] * 7, vp(FAKE), 1 << 40, None) == L.DG_EUNSUPPORTED
+    assert lib.dg_vocab_selfcond(4, 2048, 100, L.DG_BF16, *[vp(FAKE)] * 7, vp(FAKE), 16, None) == L.DG_EWORKSPACE
+    # attention
+    d = dims()
+    assert lib.dg_attn_bidir(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 1 << 40, None) == L.DG_EINVAL
+    assert lib.dg_attn_bidir(ctypes.byref(dims(head_dim=32)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                             FAKE, 1 << 40, None) == L.DG_EUNSUPPORTED
+    # renoise / init
+    assert lib.dg_renoise(0, 256, 100, FAKE, FAKE, 0.5, 1, 1, 0, FAKE, None, None) == L.DG_EINVAL
+    assert lib.dg_renoise(16, 16, 100, None, FAKE, 0.5, 1, 1, 0, FAKE, None, None) == L.DG_EINVAL
+    assert lib.dg_init_canvas(16, 16, 0, 1, 0, FAKE, None) == L.DG_EINVAL
+    # append beyond the cache capacity
+    w = L.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert lib.dg_prefill_append(ctypes.byref(dims(L=1000, cap=1024)), ctypes.byref(w), FAKE, FAKE, FAKE,
+                                 FAKE, None, FAKE, 1 << 40, None) == L.DG_EINVAL
+    assert b"cap" in lib.dg_last_error()

@@ -1,0 +1,222 @@
+"""Parity of each C-ABI entry point with the CPU oracle, element by element, at
+sizes that span several tiles with ragged tails, plus the special cases the
+method has (one-hot probabilities, flat logits, empty cache, causal prefill)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import numerics, philox, step
+from tests.gpu_util import (ATOL, RELF, argmax_match, as_f64, close, dev, f64, need_gpu,
+                            renoise_match, say, stored, top2_gap)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    import uniform_state_discrete_amd as dg
+    dg.lib()
+    yield
+
+
+# ---- renoise / initial canvas ---------------------------------------------------------
+
+@pytest.mark.parametrize("B,C,V", [(1, 16, 512), (8, 256, 262144), (3, 37, 7), (2, 100, 32768)])
+def test_renoise_bit_exact(B, C, V):
+    import uniform_state_discrete_amd as dg
+    say(f"renoise B={B} C={C} V={V}")
+    r = np.random.default_rng(B * 1000 + C)
+    R = B * C
+    a = r.integers(0, V, R).astype(np.int32)
+    c = r.random(R).astype(np.float32)
+    c[::7] = np.float32(0.9)                         # exactly tau: kept (strict <)
+    c[1::11] = np.nextafter(np.float32(0.9), np.float32(0))   # just below: renoised
+    tau, seed, t, blk = 0.9, 1002, 5, 3
+    out = torch.empty(R, dtype=torch.int32, device="cuda")
+    mask = torch.empty(R, dtype=torch.uint8, device="cuda")
+    dg.dg_renoise(R, C, V, dev(a), dev(c), tau, seed, t, blk, out, mask)
+    torch.cuda.synchronize()
+    ref_x, ref_m = step.renoise(a, c.astype(np.float64), tau, seed, t, blk, B, C, V)
+    assert np.array_equal(mask.cpu().numpy(), ref_m)
+    assert np.array_equal(out.cpu().numpy(), ref_x)
+    # the initial canvas is draw 0
+    dg.dg_init_canvas(R, C, V, seed, blk, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().reshape(B, C), step.init_canvas(seed, blk, B, C, V))
+
+
+# ---- vocabulary head / confidence / self-conditioning ------------------------------------
+
+def _vocab_inputs(R, d, V, dtype, seed, signal=None):
+    r = np.random.default_rng(seed)
+    if signal is None:   # planted-row amplitude that puts the median confidence near 1/2
+        signal = (math.sqrt(d) - math.sqrt(d - 2 * math.log(V - 1))) / 0.02
+    E = stored(r.standard_normal((V, d)).astype(np.float32) * 0.02, dtype)
+    Ef = as_f64(E, dtype)
+    y = r.integers(0, V, R)
+    amp = signal * (1 + 0.2 * r.standard_normal(R))
+    Z = amp[:, None] * Ef[y] / np.linalg.norm(Ef[y], axis=1, keepdims=True) + 0.5 * r.standard_normal((R, d))
+    Z = stored(Z, dtype)
+    return E, Z
+
+
+def _run_vocab(R, d, V, E, Z, dtype):
+    import uniform_state_discrete_amd as dg
+    Ed, Zd = dev(E), dev(Z)
+    m = torch.empty(R, dtype=torch.float32, device="cuda")
+    c = torch.empty_like(m)
+    lse = torch.empty_like(m)
+    a = torch.empty(R, dtype=torch.int32, device="cuda")
+    S = torch.empty((R, d), dtype=Zd.dtype, device="cuda")
+    ws = dg.workspace(dg.dg_vocab_workspace_bytes(R, d, V, Zd.dtype))
+    dg.dg_vocab_selfcond(R, d, V, Zd, Ed, m, a, c, lse, S, ws)
+    torch.cuda.synchronize()
+    return f64(m), a.cpu().numpy(), f64(c), f64(lse), f64(S)
+
+
+@pytest.mark.parametrize("R,d,V,dtype", [
+    (16, 64, 512, "f32"), (33, 100, 777, "f32"),          # fp32 path
+    (40, 256, 1000, "bf16"),                              # 32-row tiles: ragged rows and ids
+    (70, 128, 4133, "bf16"),
+    (256, 2048, 32768, "bf16"),                           # the 32k-vocab step's shape, every row
+    (37, 4096, 3000, "bf16"),                             # 16-row tiles (d = 4096)
+])
+def test_vocab_matches_oracle(R, d, V, dtype):
+    say(f"vocab R={R} d={d} V={V} {dtype}")
+    E, Z = _vocab_inputs(R, d, V, dtype, seed=R + d + V)
+    m, a, c, lse, S = _run_vocab(R, d, V, E, Z, dtype)
+    Ef, Zf = as_f64(E, dtype), as_f64(Z, dtype)
+    rm, ra, rlse, rc, rS = step.vocab_selfcond(Zf, Ef, dtype)
+    tol, rel = ATOL[dtype], RELF[dtype]
+    close("m", m, rm, tol)
+    close("lse", lse, rlse, tol)
+    close("c", c, rc, tol)
+    close("S", S, rS, tol, rel)
+    argmax_match("argmax", a, ra, top2_gap(Zf, Ef), rm)
+    assert 0.1 < rc.mean() < 0.95   # the inputs exercise a non-trivial softmax
+
+
+@pytest.mark.parametrize("d,V,rows", [(2048, 262144, 256), (4096, 262144, 256)])
+def test_vocab_full_vocab_sampled_rows(d, V, rows):
+    say(f"vocab full-size d={d} V={V} R={rows} (sampled rows)")
+    E, Z = _vocab_inputs(rows, d, V, "bf16", seed=d)
+    m, a, c, lse, S = _run_vocab(rows, d, V, E, Z, "bf16")
+    Ef, Zf = as_f64(E, "bf16"), as_f64(Z, "bf16")
+    idx = np.array([0, 1, 31, 32, 100, 127, 128, 200, 254, 255])
+    rm, ra, rlse, rc, rS, gap = step.vocab_rows(Zf[idx], Ef)
+    close("m", m[idx], rm, ATOL["bf16"])
+    close("lse", lse[idx], rlse, ATOL["bf16"])
+    close("c", c[idx], rc, ATOL["bf16"])
+    close("S", S[idx], numerics.round_bf16(rS), ATOL["bf16"], RELF["bf16"])
+    argmax_match("argmax", a[idx], ra, gap, rm)
+    # properties at every row: 1/V <= c <= 1, lse >= m, finite S
+    assert np.all((c >= 1.0 / V * 0.999) & (c <= 1.0 + 1e-6)) and np.all(lse >= m - 1e-4)
+    assert np.all(np.isfinite(S))
+
+
+@pytest.mark.parametrize("d,dtype", [(256, "bf16"), (2048, "bf16"), (4096, "bf16"), (64, "f32")])
+def test_vocab_one_hot_is_exact_embedding_lookup(d, dtype):
+    V, R = 3000, 40
+    r = np.random.default_rng(d)
+    E = stored(np.round(r.standard_normal((V, d)) * 0.02 * 64) / 64, dtype)
+    Ef = as_f64(E, dtype)
+    y = r.integers(0, V, R)
+    y[:4] = [0, V - 1, 1234, 31]
+    # Z = alpha * E[y] with alpha a power of two (exact) large enough that every
+    # other logit sits more than 110 below the planted one: exp underflows to 0
+    lg = Ef[y] @ Ef.T
+    own = lg[np.arange(R), y]
+    lg[np.arange(R), y] = -np.inf
+    margin = float((own - lg.max(1)).min())
+    assert margin > 0
+    alpha = 2.0 ** math.ceil(math.log2(110.0 / margin))
+    Z = stored(alpha * Ef[y], dtype)
+    assert np.array_equal(as_f64(Z, dtype), alpha * Ef[y])
+    m, a, c, lse, S = _run_vocab(R, d, V, E, Z, dtype)
+    assert np.array_equal(a, y)
+    assert np.all(c == 1.0)
+    assert np.array_equal(S, Ef[y])              # bit-exact lookup
+
+
+def test_vocab_flat_logits_closed_form():
+    V, d, R = 32768, 256, 33
+    r = np.random.default_rng(0)
+    E = stored(r.standard_normal((V, d)) * 0.02, "bf16")
+    Z = stored(np.zeros((R, d)), "bf16")
+    m, a, c, lse, S = _run_vocab(R, d, V, E, Z, "bf16")
+    assert np.all(a == 0) and np.all(m == 0)
+    assert np.all(c == np.float32(1.0 / V))     # exact: 1/V, V a power of two
+    close("lse", lse, np.full(R, math.log(V)), 1e-5)
+    close("S=mean(E)", S, np.repeat(as_f64(E, "bf16").mean(0)[None], R, 0), 2e-3)
+
+
+def test_vocab_probabilities_sum_to_one():
+    V, d, R = 5000, 512, 64
+    E, Z = _vocab_inputs(R, d, V, "bf16", seed=3)
+    Ef = as_f64(E, "bf16")
+    Ef[:, 7] = 1.0
+    E = stored(Ef, "bf16")
+    *_, S = _run_vocab(R, d, V, E, Z, "bf16")
+    close("sum_v P", S[:, 7], np.ones(R), 8e-3)
+
+
+# ---- attention ----------------------------------------------------------------------------
+
+def _attn_inputs(B, C, L, cap, Hq, Hkv, dh, dtype, seed, qscale=1.0):
+    r = np.random.default_rng(seed)
+    q = stored(r.standard_normal((B, C, Hq, dh)) * qscale, dtype)
+    Kc = stored(r.standard_normal((B, Hkv, cap, dh)), dtype)
+    Vc = stored(r.standard_normal((B, Hkv, cap, dh)), dtype)
+    Kn = stored(r.standard_normal((B, C, Hkv, dh)), dtype)
+    Vn = stored(r.standard_normal((B, C, Hkv, dh)), dtype)
+    return q, Kc, Vc, Kn, Vn
+
+
+def _run_attn(B, C, L, cap, Hq, Hkv, dh, dtype, arrs, causal):
+    import uniform_state_discrete_amd as dg
+    q, Kc, Vc, Kn, Vn = (dev(x) for x in arrs)
+    dims = dg.make_dims(B, C, L, cap, 64, Hq, Hkv, dh, 1, dg.DG_BF16 if dtype == "bf16" else dg.DG_F32)
+    out = torch.empty((B, C, Hq, dh), dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, C, Hq), dtype=torch.float32, device="cuda")
+    ws = dg.workspace(dg.dg_attn_workspace_bytes(dims))
+    dg.dg_attn_bidir(dims, q, Kc, Vc, Kn, Vn, out, lse, causal, ws)
+    torch.cuda.synchronize()
+    return f64(out), f64(lse)
+
+
+@pytest.mark.parametrize("B,C,L,Hq,Hkv,dh,dtype,qscale", [
+    (1, 16, 32, 2, 1, 32, "f32", 1.0),         # the fp32 workload's shape
+    (2, 37, 100, 4, 2, 64, "bf16", 1.0),       # ragged canvas and keys, GQA 2
+    (2, 37, 100, 4, 2, 64, "bf16", 3.0),       # sharp scores (std about 3)
+    (1, 50, 0, 8, 2, 128, "bf16", 3.0),        # empty cache, GQA 4
+    (3, 70, 333, 4, 4, 128, "bf16", 2.0),      # MHA
+    (1, 256, 1024, 16, 8, 128, "bf16", 1.0),   # the 32k-vocab step's attention shape
+])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_attention_matches_oracle(B, C, L, Hq, Hkv, dh, dtype, qscale, causal):
+    say(f"attention B={B} C={C} L={L} Hq={Hq} Hkv={Hkv} dh={dh} {dtype} q*{qscale} causal={causal}")
+    cap = L + 5
+    arrs = _attn_inputs(B, C, L, cap, Hq, Hkv, dh, dtype, seed=B + C + L + dh, qscale=qscale)
+    O, lse = _run_attn(B, C, L, cap, Hq, Hkv, dh, dtype, arrs, causal)
+    q, Kc, Vc, Kn, Vn = (as_f64(x, dtype) for x in arrs)
+    rO, rlse = step.attention(q, Kc, Vc, Kn, Vn, L, causal=bool(causal), dtype=dtype)
+    close("O", O, rO, ATOL[dtype], RELF[dtype])
+    close("lse", lse, rlse, ATOL[dtype])
+
+
+def test_attention_long_cache_sampled_rows():
+    """The 32k-token cache, 32/8-head shape (K/V ~ N(0,1)), sampled rows."""
+    B, C, L, Hq, Hkv, dh = 1, 256, 32768, 32, 8, 128
+    say("attention long cache sampled rows")
+    arrs = _attn_inputs(B, C, L, L, Hq, Hkv, dh, "bf16", seed=7, qscale=1.0)
+    O, lse = _run_attn(B, C, L, L, Hq, Hkv, dh, "bf16", arrs, 0)
+    q, Kc, Vc, Kn, Vn = (as_f64(x, "bf16") for x in arrs)
+    G = Hq // Hkv
+    for (i, h) in [(0, 0), (1, 5), (100, 31), (255, 17), (128, 8), (37, 3)]:
+        ro, rl = step.attention_row(q[0, i, h], 0, h // G, i, Kc, Vc, Kn, Vn, L, False)
+        close(f"O[{i},{h}]", O[0, i, h], numerics.round_bf16(ro), ATOL["bf16"])
+        close(f"lse[{i},{h}]", lse[0, i, h], rl, ATOL["bf16"])
+    assert np.all(np.isfinite(O))

@@ -1,0 +1,235 @@
+"""dg_denoise_step and dg_prefill_append against the oracle, in lockstep: step t
+of the oracle consumes the GPU's inputs to step t (tokens and self-conditioning
+vector), so an excluded near-tie cannot cascade.  Small workloads are compared
+on every element; the full-size workloads on sampled canvas rows (the oracle
+computes those rows one by one) plus properties that hold at every row."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import numerics, philox, step
+from synth import CONFIGS, Config, gen_problem, tau_schedule
+from tests.gpu_util import (ATOL, RELF, argmax_match, as_f64, close, close_rel, dev, f64, need_gpu,
+                            renoise_match, say, top2_gap)
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = Config("test_small_bf16", 90, B=2, C=40, L=70, d=256, Hq=4, Hkv=2, dh=64, V=3000,
+                    dtype="bf16", steps=3, blocks=2, tau=(0.6, 0.8))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    import uniform_state_discrete_amd as dg
+    dg.lib()
+    yield
+
+
+class Dev:
+    """A workload's tensors on the GPU."""
+
+    def __init__(self, p):
+        import uniform_state_discrete_amd as dg
+        c = p.cfg
+        self.cfg = c
+        self.W = {k: dev(v) for k, v in p.W.items()}
+        self.W["E"] = dev(p.E)
+        self.Kc = dev(p.Kc)
+        self.Vc = dev(p.Vc)
+        self.H = [dev(h) for h in p.H]
+        self.dt = dg.DG_BF16 if c.dtype == "bf16" else dg.DG_F32
+        self.dims = dg.make_dims(c.B, c.C, c.L, c.cap, c.d, c.Hq, c.Hkv, c.dh, c.V, self.dt)
+        self.ws = dg.workspace(dg.dg_workspace_bytes(self.dims))
+
+    def step(self, x, S, tau, t, block, L=None):
+        import uniform_state_discrete_amd as dg
+        c = self.cfg
+        R = c.B * c.C
+        fdt = self.W["E"].dtype
+        o = dict(
+            H=self.H[block], k_cache=self.Kc, v_cache=self.Vc, tokens_in=x, selfcond_in=S,
+            tokens_out=torch.empty_like(x), selfcond_out=torch.empty((c.B, c.C, c.d), dtype=fdt, device="cuda"),
+            max_logit=torch.empty(R, dtype=torch.float32, device="cuda"),
+            conf=torch.empty(R, dtype=torch.float32, device="cuda"),
+            lse=torch.empty(R, dtype=torch.float32, device="cuda"),
+            argmax=torch.empty(R, dtype=torch.int32, device="cuda"),
+            mask=torch.empty(R, dtype=torch.uint8, device="cuda"),
+            x_out=torch.empty((R, c.d), dtype=fdt, device="cuda"),
+            q_out=torch.empty((R, c.Hq * c.dh), dtype=fdt, device="cuda"),
+            k_new_out=torch.empty((R, c.Hkv * c.dh), dtype=fdt, device="cuda"),
+            v_new_out=torch.empty((R, c.Hkv * c.dh), dtype=fdt, device="cuda"),
+            attn_out=torch.empty((R, c.Hq * c.dh), dtype=fdt, device="cuda"),
+            z_out=torch.empty((R, c.d), dtype=fdt, device="cuda"))
+        dims = self.dims if L is None else dg.make_dims(c.B, c.C, L, c.cap, c.d, c.Hq, c.Hkv, c.dh, c.V, self.dt)
+        dg.dg_denoise_step(dims, self.W, o, tau, c.seed, t, block, self.ws)
+        torch.cuda.synchronize()
+        return o
+
+
+def host(p):
+    c = p.cfg
+    f = lambda a: as_f64(a, c.dtype)
+    return dict(E=f(p.E), W={k: f(v) for k, v in p.W.items()}, Kc=f(p.Kc), Vc=f(p.Vc),
+                H=[f(h) for h in p.H])
+
+
+def compare_full(c, o, ref, E, tau, tag):
+    dt = c.dtype
+    R = c.B * c.C
+    rel_ulp = 2.0 ** -7 if dt == "bf16" else 1e-6
+    close_rel(f"{tag} X", f64(o["x_out"]), ref["X"].reshape(R, -1), rel_ulp)
+    close_rel(f"{tag} Q", f64(o["q_out"]), ref["Q"].reshape(R, -1), 2 * rel_ulp)
+    close_rel(f"{tag} Kn", f64(o["k_new_out"]), ref["Kn"].reshape(R, -1), 2 * rel_ulp)
+    close_rel(f"{tag} Vn", f64(o["v_new_out"]), ref["Vn"].reshape(R, -1), 2 * rel_ulp)
+    close(f"{tag} O", f64(o["attn_out"]), ref["O"].reshape(R, -1), ATOL[dt], RELF[dt])
+    close(f"{tag} Z", f64(o["z_out"]), ref["Z"].reshape(R, -1), ATOL[dt] if dt == "bf16" else 4 * ATOL[dt])
+    close(f"{tag} m", f64(o["max_logit"]), ref["m"], ATOL[dt])
+    close(f"{tag} lse", f64(o["lse"]), ref["lse"], ATOL[dt])
+    close(f"{tag} c", f64(o["conf"]), ref["c"], ATOL[dt])
+    close(f"{tag} S", f64(o["selfcond_out"]).reshape(R, -1), ref["S"].reshape(R, -1), ATOL[dt], RELF[dt])
+    gap = top2_gap(ref["Z"].reshape(R, -1), E)
+    argmax_match(f"{tag} argmax", o["argmax"].cpu().numpy(), ref["a"], gap, ref["m"])
+    tie = gap < 1e-3 * np.maximum(1.0, np.abs(ref["m"]))
+    renoise_match(f"{tag} renoise", o["tokens_out"].cpu().numpy(), o["mask"].cpu().numpy(),
+                  ref["x_new"], ref["mask"], ref["c"], tau, extra_excl=tie)
+
+
+@pytest.mark.parametrize("cfg", [CONFIGS[0], SMALL_BF16, CONFIGS[1]], ids=lambda c: c.name)
+def test_step_lockstep_every_element(cfg):
+    import uniform_state_discrete_amd as dg
+    say(f"step lockstep {cfg.name}")
+    p = gen_problem(cfg)
+    g = Dev(p)
+    h = host(p)
+    taus = tau_schedule(cfg)
+    x = torch.empty((cfg.B, cfg.C), dtype=torch.int32, device="cuda")
+    dg.dg_init_canvas(cfg.R, cfg.C, cfg.V, cfg.seed, 0, x)
+    S = None
+    nsteps = min(cfg.steps, 4)
+    kept = []
+    for s in range(nsteps):
+        o = g.step(x, S, taus[s], s + 1, 0)
+        xin = x.cpu().numpy()
+        Sin = None if S is None else f64(S)
+        ref = step.denoise_step(h["H"][0], h["E"], h["W"], h["Kc"], h["Vc"], cfg.L, xin, Sin,
+                                taus[s], cfg.seed, s + 1, 0, cfg.dtype)
+        compare_full(cfg, o, ref, h["E"], taus[s], f"step {s}")
+        kept.append(1 - ref["mask"].mean())
+        x, S = o["tokens_out"], o["selfcond_out"]
+    say("kept fraction per step", np.round(kept, 3))
+
+
+# ---- full-size workloads, sampled rows ---------------------------------------------------
+
+def oracle_rows(h, c, L, xin, Sin, tau, t, block, rows):
+    """The oracle step restricted to the given rows (b*C + i).  Projections are
+    computed for every row (the keys need them); attention, Z, the vocabulary
+    head and renoise only for the sampled rows."""
+    dt = c.dtype
+    R = c.B * c.C
+    X = step.assemble(h["H"][block], h["E"], xin, Sin, dt).reshape(R, c.d)
+    Q = step.linear(X, h["W"]["Wq"], dt).reshape(c.B, c.C, c.Hq, c.dh)
+    Kn = step.linear(X, h["W"]["Wk"], dt).reshape(c.B, c.C, c.Hkv, c.dh)
+    Vn = step.linear(X, h["W"]["Wv"], dt).reshape(c.B, c.C, c.Hkv, c.dh)
+    O = np.empty((len(rows), c.Hq * c.dh))
+    for n, r in enumerate(rows):
+        b, i = divmod(int(r), c.C)
+        for hh in range(c.Hq):
+            o, _ = step.attention_row(Q[b, i, hh], b, hh // c.G, i, h["Kc"], h["Vc"], Kn, Vn, L, False)
+            O[n, hh * c.dh:(hh + 1) * c.dh] = o
+    O = numerics.round_store(O, dt)
+    Z = numerics.round_store(X[rows] + O @ h["W"]["Wo"].T, dt)
+    m, a, lse, cc, S, gap = step.vocab_rows(Z, h["E"])
+    S = numerics.round_store(S, dt)
+    tau32 = float(np.float32(tau))
+    mask = cc < tau32
+    xn = np.array([philox.uniform_token(c.seed, t, int(r) // c.C, block, int(r) % c.C, c.V) if mk else ai
+                   for r, mk, ai in zip(rows, mask, a)])
+    return dict(X=X, Q=Q.reshape(R, -1), Kn=Kn.reshape(R, -1), Vn=Vn.reshape(R, -1), O=O, Z=Z,
+                m=m, a=a, lse=lse, c=cc, S=S, gap=gap, x_new=xn, mask=mask.astype(np.uint8))
+
+
+def compare_rows(c, o, ref, rows, tau, tag):
+    dt = c.dtype
+    close_rel(f"{tag} X", f64(o["x_out"]), ref["X"], 2.0 ** -7)
+    close_rel(f"{tag} Q", f64(o["q_out"]), ref["Q"], 2.0 ** -6)
+    close_rel(f"{tag} Kn", f64(o["k_new_out"]), ref["Kn"], 2.0 ** -6)
+    close_rel(f"{tag} Vn", f64(o["v_new_out"]), ref["Vn"], 2.0 ** -6)
+    close(f"{tag} O", f64(o["attn_out"])[rows], ref["O"], ATOL[dt], RELF[dt])
+    close(f"{tag} Z", f64(o["z_out"])[rows], ref["Z"], ATOL[dt])
+    close(f"{tag} m", f64(o["max_logit"])[rows], ref["m"], ATOL[dt])
+    close(f"{tag} lse", f64(o["lse"])[rows], ref["lse"], ATOL[dt])
+    close(f"{tag} c", f64(o["conf"])[rows], ref["c"], ATOL[dt])
+    close(f"{tag} S", f64(o["selfcond_out"]).reshape(c.R, -1)[rows], ref["S"], ATOL[dt], RELF[dt])
+    argmax_match(f"{tag} argmax", o["argmax"].cpu().numpy()[rows], ref["a"], ref["gap"], ref["m"])
+    tie = ref["gap"] < 1e-3 * np.maximum(1.0, np.abs(ref["m"]))
+    renoise_match(f"{tag} renoise", o["tokens_out"].cpu().numpy().reshape(-1)[rows],
+                  o["mask"].cpu().numpy()[rows], ref["x_new"], ref["mask"], ref["c"], tau, extra_excl=tie)
+    # properties at every row
+    cf = f64(o["conf"])
+    assert np.all((cf >= 1.0 / c.V * 0.999) & (cf <= 1.0 + 1e-6))
+    assert np.all(np.isfinite(f64(o["selfcond_out"])))
+    tok = o["tokens_out"].cpu().numpy().reshape(-1)
+    assert tok.min() >= 0 and tok.max() < c.V
+    keep = o["mask"].cpu().numpy() == 0
+    assert np.array_equal(tok[keep], o["argmax"].cpu().numpy()[keep])
+    assert np.all(cf[keep] >= np.float32(tau)) and np.all(cf[~keep] < np.float32(tau))
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_step_full_size_sampled_rows(idx):
+    import uniform_state_discrete_amd as dg
+    c = CONFIGS[idx]
+    say(f"full-size step {c.name}")
+    p = gen_problem(c)
+    g = Dev(p)
+    h = host(p)
+    del p
+    taus = tau_schedule(c)
+    x = torch.empty((c.B, c.C), dtype=torch.int32, device="cuda")
+    dg.dg_init_canvas(c.R, c.C, c.V, c.seed, 0, x)
+    rng = np.random.default_rng(idx)
+    rows = np.unique(np.concatenate([[0, 31, 32, c.R - 1], rng.integers(0, c.R, 8)]))
+    S = None
+    for s in range(2):
+        o = g.step(x, S, taus[s], s + 1, 0)
+        ref = oracle_rows(h, c, c.L, x.cpu().numpy(), None if S is None else f64(S), taus[s], s + 1, 0, rows)
+        compare_rows(c, o, ref, rows, taus[s], f"step {s}")
+        x, S = o["tokens_out"], o["selfcond_out"]
+
+
+@pytest.mark.parametrize("cfg", [CONFIGS[0], SMALL_BF16], ids=lambda c: c.name)
+def test_block_append_and_next_block(cfg):
+    """Finish block 0, append it through the causal prefill, then run a step of
+    block 1 against the grown cache."""
+    import uniform_state_discrete_amd as dg
+    say(f"block append {cfg.name}")
+    c = cfg if cfg.blocks > 1 else Config(cfg.name + "_2blk", cfg.index, cfg.B, cfg.C, cfg.L, cfg.d,
+                                          cfg.Hq, cfg.Hkv, cfg.dh, cfg.V, cfg.dtype, cfg.steps, 2, cfg.tau)
+    p = gen_problem(c)
+    g = Dev(p)
+    h = host(p)
+    x = torch.empty((c.B, c.C), dtype=torch.int32, device="cuda")
+    dg.dg_init_canvas(c.R, c.C, c.V, c.seed, 0, x)
+    o = g.step(x, None, c.tau[0], 1, 0)
+    xf = o["argmax"].view(c.B, c.C).contiguous()        # the finalized canvas: argmax of the last step
+    attn = torch.empty((c.B, c.C, c.Hq, c.dh), dtype=g.W["E"].dtype, device="cuda")
+    Kc0, Vc0 = f64(g.Kc), f64(g.Vc)
+    dg.dg_prefill_append(g.dims, g.W, g.H[0], xf, g.Kc, g.Vc, attn, g.ws)
+    torch.cuda.synchronize()
+    K2, V2, rO, _ = step.prefill_append(h["H"][0], h["E"], h["W"], Kc0, Vc0, c.L, xf.cpu().numpy(), c.dtype)
+    assert np.array_equal(f64(g.Kc)[:, :, :c.L], Kc0[:, :, :c.L])
+    close_rel("appended K", f64(g.Kc)[:, :, c.L:c.L + c.C], K2[:, :, c.L:c.L + c.C], 2.0 ** -6)
+    close_rel("appended V", f64(g.Vc)[:, :, c.L:c.L + c.C], V2[:, :, c.L:c.L + c.C], 2.0 ** -6)
+    close("causal O", f64(attn), rO, ATOL[c.dtype], RELF[c.dtype])
+    # block 1 starts from a fresh canvas (draw 0 of block 1) over the grown cache
+    L1 = c.L + c.C
+    dg.dg_init_canvas(c.R, c.C, c.V, c.seed, 1, x)
+    assert np.array_equal(x.cpu().numpy(), step.init_canvas(c.seed, 1, c.B, c.C, c.V))
+    o = g.step(x, None, c.tau[1], 1, 1, L=L1)
+    ref = step.denoise_step(h["H"][1], h["E"], h["W"], f64(g.Kc), f64(g.Vc), L1, x.cpu().numpy(), None,
+                            c.tau[1], c.seed, 1, 1, c.dtype)
+    compare_full(c, o, ref, h["E"], c.tau[1], "block 1 step 0")

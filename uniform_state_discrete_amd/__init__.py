@@ -1,0 +1,16 @@
+"""MI355X-native canvas denoise step of uniform-state text diffusion.
+
+The computation lives in libdg.so (hand-written HIP kernels for gfx950 behind
+the C ABI of include/dg.h); this package is its Python binding.  Importing it
+does not touch the GPU; the library is loaded on first use and a missing
+library is an error, never a fallback.
+"""
+from ._lib import (  # noqa: F401
+    DG_BF16, DG_F32, DG_OK, DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE, DG_EHIP,
+    DgError, Dims, Weights, StepIO, STEP_IO_FIELDS, LIB_PATH,
+    lib, make_dims, workspace, ptr, dtype_code, stream_handle,
+    dg_workspace_bytes, dg_attn_workspace_bytes, dg_vocab_workspace_bytes,
+    dg_denoise_step, dg_attn_bidir, dg_vocab_selfcond, dg_renoise, dg_init_canvas,
+    dg_prefill_append,
+)
+from .device import to_device, torch_dtype  # noqa: F401

@@ -1,0 +1,201 @@
+"""ctypes binding of libdg (include/dg.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls and takes
+torch tensors that already live on the GPU; it checks dtype / device /
+contiguity, passes raw pointers and sizes, and raises DgError on a negative
+status.  No step of the computation runs in Python.  torch is used for device
+memory and streams only.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdg.so")
+
+DG_F32, DG_BF16 = 0, 1
+DG_OK, DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE, DG_EHIP = 0, -1, -2, -3, -4
+
+
+class DgError(RuntimeError):
+    def __init__(self, status, where, detail):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {detail}")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "C", "L", "cap", "d", "n_q_heads", "n_kv_heads", "head_dim", "V", "dtype")]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("Wq", "Wk", "Wv", "Wo", "E")]
+
+
+STEP_IO_FIELDS = ("H", "k_cache", "v_cache", "tokens_in", "selfcond_in", "tokens_out",
+                  "selfcond_out", "max_logit", "conf", "lse", "argmax", "mask",
+                  "x_out", "q_out", "k_new_out", "v_new_out", "attn_out", "z_out")
+
+
+class StepIO(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in STEP_IO_FIELDS]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libdg.so.  Raises if it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m uniform_state_discrete_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32, u32, u64, f32 = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                      ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float)
+        pd = ctypes.POINTER(Dims)
+        sig = {
+            "dg_workspace_bytes": (sz, [pd]),
+            "dg_attn_workspace_bytes": (sz, [pd]),
+            "dg_vocab_workspace_bytes": (sz, [i32, i32, i32, i32]),
+            "dg_denoise_step": (ctypes.c_int, [pd, ctypes.POINTER(Weights), ctypes.POINTER(StepIO),
+                                               f32, u64, u32, u32, vp, sz, vp]),
+            "dg_attn_bidir": (ctypes.c_int, [pd, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]),
+            "dg_vocab_selfcond": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                                 vp, sz, vp]),
+            "dg_renoise": (ctypes.c_int, [i32, i32, i32, vp, vp, f32, u64, u32, u32, vp, vp, vp]),
+            "dg_init_canvas": (ctypes.c_int, [i32, i32, i32, u64, u32, vp, vp]),
+            "dg_prefill_append": (ctypes.c_int, [pd, ctypes.POINTER(Weights), vp, vp, vp, vp, vp,
+                                                 vp, sz, vp]),
+            "dg_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+            "dg_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status, where):
+    if status != DG_OK:
+        L = lib()
+        raise DgError(status, where, f"{L.dg_status_str(status).decode()} -- {L.dg_last_error().decode()}")
+
+
+def dtype_code(t):
+    if t == torch.bfloat16:
+        return DG_BF16
+    if t == torch.float32:
+        return DG_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def ptr(t, dtype=None):
+    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def stream_handle(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def make_dims(B, C, L, cap, d, n_q_heads, n_kv_heads, head_dim, V, dtype):
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return Dims(B, C, L, cap, d, n_q_heads, n_kv_heads, head_dim, V, code)
+
+
+def workspace(nbytes, device="cuda"):
+    return torch.empty(max(1, int(nbytes)), dtype=torch.uint8, device=device)
+
+
+# ---- entry points ----------------------------------------------------------------
+
+def dg_workspace_bytes(dims):
+    return lib().dg_workspace_bytes(ctypes.byref(dims))
+
+
+def dg_attn_workspace_bytes(dims):
+    return lib().dg_attn_workspace_bytes(ctypes.byref(dims))
+
+
+def dg_vocab_workspace_bytes(rows, d, V, dtype):
+    return lib().dg_vocab_workspace_bytes(rows, d, V, dtype if isinstance(dtype, int) else dtype_code(dtype))
+
+
+_FLOAT_IO = ("H", "k_cache", "v_cache", "selfcond_in", "selfcond_out", "x_out", "q_out",
+             "k_new_out", "v_new_out", "attn_out", "z_out")
+
+
+def _check_float_dtype(dims, tensors):
+    want = torch.bfloat16 if dims.dtype == DG_BF16 else torch.float32
+    for name, t in tensors:
+        if t is not None and t.dtype != want:
+            raise TypeError(f"{name}: expected {want}, got {t.dtype}")
+
+
+def dg_denoise_step(dims, weights, io, tau, seed, t, block, ws, stream=None):
+    """weights: dict Wq, Wk, Wv, Wo, E; io: dict with the dg_step_io fields
+    (missing keys -> NULL).  ws: uint8 workspace tensor."""
+    _check_float_dtype(dims, [(k, weights.get(k)) for k in ("Wq", "Wk", "Wv", "Wo", "E")] +
+                       [(k, io.get(k)) for k in _FLOAT_IO])
+    for k in ("tokens_in", "tokens_out", "argmax"):
+        if io.get(k) is not None and io[k].dtype != torch.int32:
+            raise TypeError(f"{k}: expected torch.int32")
+    w = Weights(*(ptr(weights[k]) for k in ("Wq", "Wk", "Wv", "Wo", "E")))
+    s = StepIO(*(ptr(io.get(k)) for k in STEP_IO_FIELDS))
+    st = lib().dg_denoise_step(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(s), float(tau),
+                               int(seed), int(t), int(block), ptr(ws), ws.numel() if ws is not None else 0,
+                               stream_handle(stream))
+    _check(st, "dg_denoise_step")
+
+
+def dg_attn_bidir(dims, q, k_cache, v_cache, k_new, v_new, out, lse_out, causal, ws, stream=None):
+    st = lib().dg_attn_bidir(ctypes.byref(dims), ptr(q), ptr(k_cache), ptr(v_cache), ptr(k_new),
+                             ptr(v_new), ptr(out), ptr(lse_out, torch.float32), int(bool(causal)),
+                             ptr(ws), ws.numel() if ws is not None else 0, stream_handle(stream))
+    _check(st, "dg_attn_bidir")
+
+
+def dg_vocab_selfcond(rows, d, V, z, E, max_logit, argmax, conf, lse, selfcond, ws, stream=None):
+    st = lib().dg_vocab_selfcond(int(rows), int(d), int(V), dtype_code(z.dtype), ptr(z), ptr(E),
+                                 ptr(max_logit, torch.float32), ptr(argmax, torch.int32),
+                                 ptr(conf, torch.float32), ptr(lse, torch.float32), ptr(selfcond),
+                                 ptr(ws), ws.numel() if ws is not None else 0, stream_handle(stream))
+    _check(st, "dg_vocab_selfcond")
+
+
+def dg_renoise(rows, canvas, V, argmax, conf, tau, seed, t, block, tokens_out, mask_out, stream=None):
+    st = lib().dg_renoise(int(rows), int(canvas), int(V), ptr(argmax, torch.int32),
+                          ptr(conf, torch.float32), float(tau), int(seed), int(t), int(block),
+                          ptr(tokens_out, torch.int32), ptr(mask_out, torch.uint8), stream_handle(stream))
+    _check(st, "dg_renoise")
+
+
+def dg_init_canvas(rows, canvas, V, seed, block, tokens_out, stream=None):
+    st = lib().dg_init_canvas(int(rows), int(canvas), int(V), int(seed), int(block),
+                              ptr(tokens_out, torch.int32), stream_handle(stream))
+    _check(st, "dg_init_canvas")
+
+
+def dg_prefill_append(dims, weights, H, tokens_final, k_cache, v_cache, attn_out, ws, stream=None):
+    w = Weights(*(ptr(weights.get(k)) for k in ("Wq", "Wk", "Wv", "Wo", "E")))
+    st = lib().dg_prefill_append(ctypes.byref(dims), ctypes.byref(w), ptr(H), ptr(tokens_final, torch.int32),
+                                 ptr(k_cache), ptr(v_cache), ptr(attn_out), ptr(ws),
+                                 ws.numel() if ws is not None else 0, stream_handle(stream))
+    _check(st, "dg_prefill_append")

@@ -1,0 +1,294 @@
+// C ABI of libdg: argument checks (before anything is enqueued), workspace
+// layout and the launch sequence of the canvas denoise step.
+#include "../../include/dg.h"
+#include "dg_common.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(DG_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t esize(int dtype) { return dtype == DG_BF16 ? 2 : 4; }
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Limits of what is implemented.
+constexpr int kMaxSplits = 1024;
+
+int check_dims(const dg_dims* d, bool need_vocab) {
+  if (!d) return fail(DG_EINVAL, "dims is NULL");
+  if (d->dtype != DG_F32 && d->dtype != DG_BF16) return fail(DG_EINVAL, "dtype %d is not DG_F32 or DG_BF16", d->dtype);
+  if (d->B <= 0 || d->C <= 0 || d->d <= 0 || d->n_q_heads <= 0 || d->n_kv_heads <= 0 ||
+      d->head_dim <= 0 || (need_vocab && d->V <= 0))
+    return fail(DG_EINVAL, "sizes must be positive (B=%d C=%d d=%d Hq=%d Hkv=%d dh=%d V=%d)", d->B, d->C,
+                d->d, d->n_q_heads, d->n_kv_heads, d->head_dim, d->V);
+  if (d->L < 0 || d->cap < d->L) return fail(DG_EINVAL, "need 0 <= L <= cap (L=%d cap=%d)", d->L, d->cap);
+  if (d->n_q_heads % d->n_kv_heads) return fail(DG_EINVAL, "n_q_heads %% n_kv_heads != 0 (%d, %d)", d->n_q_heads, d->n_kv_heads);
+  if ((long long)d->B * d->C > (1 << 24) || (long long)d->L + d->C > (1 << 28))
+    return fail(DG_EUNSUPPORTED, "B*C or L+C too large");
+  if (d->dtype == DG_BF16) {
+    if (d->head_dim != 64 && d->head_dim != 128) return fail(DG_EUNSUPPORTED, "bf16 head_dim must be 64 or 128 (got %d)", d->head_dim);
+    if (d->n_kv_heads * d->head_dim % 64) return fail(DG_EUNSUPPORTED, "bf16 needs n_kv_heads*head_dim %% 64 == 0");
+  } else {
+    if (d->head_dim > 256) return fail(DG_EUNSUPPORTED, "fp32 head_dim must be <= 256 (got %d)", d->head_dim);
+  }
+  return DG_OK;
+}
+
+int check_vocab_shape(int rows, int d, int V, int dtype) {
+  if (rows <= 0 || d <= 0 || V <= 0) return fail(DG_EINVAL, "rows, d, V must be positive (%d, %d, %d)", rows, d, V);
+  if (dtype != DG_F32 && dtype != DG_BF16) return fail(DG_EINVAL, "dtype %d is not DG_F32 or DG_BF16", dtype);
+  if (dtype == DG_BF16) {
+    if (!(d == 128 || d == 256 || d == 512 || d == 1024 || d == 2048 || d == 4096))
+      return fail(DG_EUNSUPPORTED, "bf16 vocab head needs d in {128,256,512,1024,2048,4096} (got %d)", d);
+    dg::VocabPlan p = dg::vocab_plan(rows, d, V, dtype);
+    if (p.nsplit > kMaxSplits) return fail(DG_EUNSUPPORTED, "too many vocab splits");
+  } else {
+    if (d > 4096) return fail(DG_EUNSUPPORTED, "fp32 vocab head needs d <= 4096 (got %d)", d);
+  }
+  return DG_OK;
+}
+
+size_t vocab_ws(int rows, int d, int V, int dtype) {
+  dg::VocabPlan p = dg::vocab_plan(rows, d, V, dtype);
+  return round_up(p.part_S_bytes) + round_up(p.part_stat_bytes);
+}
+
+size_t attn_ws(const dg_dims* d, int causal) {
+  dg::AttnPlan p = dg::attn_plan(d->B, d->C, d->L, d->cap, d->n_q_heads, d->n_kv_heads, d->head_dim,
+                                 d->dtype, causal);
+  return round_up(p.part_bytes);
+}
+
+// Step workspace: X | Q | Kn | Vn | O | Z | scratch (max of attention and vocab partials).
+struct StepLayout {
+  size_t X, Q, Kn, Vn, O, Z, scratch, total;
+};
+StepLayout step_layout(const dg_dims* d) {
+  const size_t R = (size_t)d->B * d->C, es = esize(d->dtype);
+  StepLayout s{};
+  size_t off = 0;
+  s.X = off; off += round_up(R * d->d * es);
+  s.Q = off; off += round_up(R * d->n_q_heads * d->head_dim * es);
+  s.Kn = off; off += round_up(R * d->n_kv_heads * d->head_dim * es);
+  s.Vn = off; off += round_up(R * d->n_kv_heads * d->head_dim * es);
+  s.O = off; off += round_up(R * d->n_q_heads * d->head_dim * es);
+  s.Z = off; off += round_up(R * d->d * es);
+  s.scratch = off;
+  size_t sc = attn_ws(d, 0);
+  const size_t sc1 = attn_ws(d, 1);
+  if (sc1 > sc) sc = sc1;
+  if (d->V > 0) {
+    const size_t sv = vocab_ws((int)R, d->d, d->V, d->dtype);
+    if (sv > sc) sc = sv;
+  }
+  s.total = off + sc;
+  return s;
+}
+
+int check_bf16_align(const dg_dims* d, const void* const* ptrs, int n) {
+  if (d->dtype != DG_BF16) return DG_OK;
+  for (int i = 0; i < n; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i])) return fail(DG_EINVAL, "bf16 tensor pointer #%d is not 16-byte aligned", i);
+  return DG_OK;
+}
+
+char* at(void* ws, size_t off) { return (char*)ws + off; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dg_status_str(int status) {
+  switch (status) {
+    case DG_OK: return "DG_OK";
+    case DG_EINVAL: return "DG_EINVAL: invalid argument";
+    case DG_EUNSUPPORTED: return "DG_EUNSUPPORTED: valid but not implemented";
+    case DG_EWORKSPACE: return "DG_EWORKSPACE: workspace missing or too small";
+    case DG_EHIP: return "DG_EHIP: HIP call failed";
+    default: return "unknown dg_status";
+  }
+}
+
+const char* dg_last_error(void) { return g_err; }
+
+size_t dg_workspace_bytes(const dg_dims* dims) {
+  if (check_dims(dims, true) != DG_OK) return 0;
+  return step_layout(dims).total;
+}
+
+size_t dg_attn_workspace_bytes(const dg_dims* dims) {
+  if (check_dims(dims, false) != DG_OK) return 0;
+  const size_t a = attn_ws(dims, 0), b = attn_ws(dims, 1);
+  return a > b ? a : b;
+}
+
+size_t dg_vocab_workspace_bytes(int32_t rows, int32_t d, int32_t V, int32_t dtype) {
+  if (check_vocab_shape(rows, d, V, dtype) != DG_OK) return 0;
+  return vocab_ws(rows, d, V, dtype);
+}
+
+int dg_renoise(int32_t rows, int32_t canvas, int32_t V, const int32_t* argmax, const float* conf,
+               float tau, uint64_t seed, uint32_t t, uint32_t block, int32_t* tokens_out,
+               uint8_t* mask_out, void* stream) {
+  if (rows <= 0 || canvas <= 0 || V <= 0) return fail(DG_EINVAL, "rows, canvas, V must be positive (%d, %d, %d)", rows, canvas, V);
+  if (!argmax || !conf || !tokens_out) return fail(DG_EINVAL, "argmax, conf and tokens_out must be non-NULL");
+  hipError_t e = dg::launch_renoise(rows, canvas, V, argmax, conf, tau, seed, t, block, tokens_out,
+                                    mask_out, (hipStream_t)stream);
+  return e == hipSuccess ? DG_OK : hip_fail(e, "dg_renoise");
+}
+
+int dg_init_canvas(int32_t rows, int32_t canvas, int32_t V, uint64_t seed, uint32_t block,
+                   int32_t* tokens_out, void* stream) {
+  if (rows <= 0 || canvas <= 0 || V <= 0) return fail(DG_EINVAL, "rows, canvas, V must be positive (%d, %d, %d)", rows, canvas, V);
+  if (!tokens_out) return fail(DG_EINVAL, "tokens_out must be non-NULL");
+  hipError_t e = dg::launch_renoise(rows, canvas, V, nullptr, nullptr, 0.f, seed, 0, block,
+                                    tokens_out, nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? DG_OK : hip_fail(e, "dg_init_canvas");
+}
+
+int dg_vocab_selfcond(int32_t rows, int32_t d, int32_t V, int32_t dtype, const void* z,
+                      const void* E, float* max_logit, int32_t* argmax, float* conf, float* lse,
+                      void* selfcond, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_vocab_shape(rows, d, V, dtype);
+  if (st != DG_OK) return st;
+  if (!z || !E || !max_logit || !argmax || !conf || !selfcond)
+    return fail(DG_EINVAL, "z, E, max_logit, argmax, conf and selfcond must be non-NULL");
+  if (dtype == DG_BF16 && (!aligned16(z) || !aligned16(E) || !aligned16(selfcond)))
+    return fail(DG_EINVAL, "bf16 z, E and selfcond must be 16-byte aligned");
+  const size_t need = vocab_ws(rows, d, V, dtype);
+  if (need && (!ws || ws_bytes < need))
+    return fail(DG_EWORKSPACE, "vocab workspace needs %zu bytes (got %zu)", need, ws ? ws_bytes : 0);
+  dg::VocabPlan p = dg::vocab_plan(rows, d, V, dtype);
+  hipError_t e = dg::launch_vocab(p, z, E, max_logit, argmax, conf, lse, selfcond, ws, (hipStream_t)stream);
+  return e == hipSuccess ? DG_OK : hip_fail(e, "dg_vocab_selfcond");
+}
+
+int dg_attn_bidir(const dg_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                  const void* k_new, const void* v_new, void* out, float* lse_out, int causal,
+                  void* ws, size_t ws_bytes, void* stream) {
+  int st = check_dims(dims, false);
+  if (st != DG_OK) return st;
+  if (!q || !k_new || !v_new || !out || (dims->L > 0 && (!k_cache || !v_cache)))
+    return fail(DG_EINVAL, "q, k_new, v_new, out (and the caches when L > 0) must be non-NULL");
+  const void* ptrs[] = {q, k_cache, v_cache, k_new, v_new, out};
+  if ((st = check_bf16_align(dims, ptrs, 6)) != DG_OK) return st;
+  const size_t need = attn_ws(dims, causal ? 1 : 0);
+  if (need && (!ws || ws_bytes < need))
+    return fail(DG_EWORKSPACE, "attention workspace needs %zu bytes (got %zu)", need, ws ? ws_bytes : 0);
+  dg::AttnPlan p = dg::attn_plan(dims->B, dims->C, dims->L, dims->cap, dims->n_q_heads, dims->n_kv_heads,
+                                 dims->head_dim, dims->dtype, causal ? 1 : 0);
+  hipError_t e = dg::launch_attn(p, q, k_cache, v_cache, k_new, v_new, out, lse_out, ws, (hipStream_t)stream);
+  return e == hipSuccess ? DG_OK : hip_fail(e, "dg_attn_bidir");
+}
+
+int dg_denoise_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io, float tau,
+                    uint64_t seed, uint32_t t, uint32_t block, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int st = check_dims(dims, true);
+  if (st != DG_OK) return st;
+  if (!w || !io) return fail(DG_EINVAL, "weights and io must be non-NULL");
+  if (!w->Wq || !w->Wk || !w->Wv || !w->Wo || !w->E) return fail(DG_EINVAL, "every weight pointer must be non-NULL");
+  if (!io->H || !io->tokens_in || !io->tokens_out || !io->selfcond_out || !io->max_logit ||
+      !io->conf || !io->argmax || (dims->L > 0 && (!io->k_cache || !io->v_cache)))
+    return fail(DG_EINVAL, "H, tokens_in/out, selfcond_out, max_logit, conf, argmax (and the caches when L > 0) must be non-NULL");
+  const int R = dims->B * dims->C;
+  if ((st = check_vocab_shape(R, dims->d, dims->V, dims->dtype)) != DG_OK) return st;
+  if (dims->dtype == DG_BF16 && (dims->d % 128 || dims->n_q_heads * dims->head_dim % 64))
+    return fail(DG_EUNSUPPORTED, "bf16 step needs d %% 128 == 0 and n_q_heads*head_dim %% 64 == 0");
+  const void* ptrs[] = {w->Wq, w->Wk, w->Wv, w->Wo, w->E, io->H, io->k_cache, io->v_cache,
+                        io->selfcond_in, io->selfcond_out, io->x_out, io->q_out, io->k_new_out,
+                        io->v_new_out, io->attn_out, io->z_out};
+  if ((st = check_bf16_align(dims, ptrs, 16)) != DG_OK) return st;
+  const StepLayout L = step_layout(dims);
+  if (!ws || ws_bytes < L.total)
+    return fail(DG_EWORKSPACE, "step workspace needs %zu bytes (got %zu)", L.total, ws ? ws_bytes : 0);
+  if (!aligned16(ws)) return fail(DG_EINVAL, "workspace must be 16-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = dims->dtype, d = dims->d, Hq = dims->n_q_heads, Hkv = dims->n_kv_heads, dh = dims->head_dim;
+  void* X = io->x_out ? io->x_out : at(ws, L.X);
+  void* Q = io->q_out ? io->q_out : at(ws, L.Q);
+  void* Kn = io->k_new_out ? io->k_new_out : at(ws, L.Kn);
+  void* Vn = io->v_new_out ? io->v_new_out : at(ws, L.Vn);
+  void* O = io->attn_out ? io->attn_out : at(ws, L.O);
+  void* Z = io->z_out ? io->z_out : at(ws, L.Z);
+  void* scratch = at(ws, L.scratch);
+  hipError_t e;
+  if ((e = dg::launch_assemble(dt, R, d, dims->V, io->H, w->E, io->tokens_in, io->selfcond_in, X, s)) != hipSuccess)
+    return hip_fail(e, "assemble");
+  if ((e = dg::launch_gemm_nt(dt, R, Hq * dh, d, X, w->Wq, nullptr, Q, s)) != hipSuccess) return hip_fail(e, "Q projection");
+  if ((e = dg::launch_gemm_nt(dt, R, Hkv * dh, d, X, w->Wk, nullptr, Kn, s)) != hipSuccess) return hip_fail(e, "K projection");
+  if ((e = dg::launch_gemm_nt(dt, R, Hkv * dh, d, X, w->Wv, nullptr, Vn, s)) != hipSuccess) return hip_fail(e, "V projection");
+  dg::AttnPlan ap = dg::attn_plan(dims->B, dims->C, dims->L, dims->cap, Hq, Hkv, dh, dt, 0);
+  if ((e = dg::launch_attn(ap, Q, io->k_cache, io->v_cache, Kn, Vn, O, nullptr, scratch, s)) != hipSuccess)
+    return hip_fail(e, "attention");
+  if ((e = dg::launch_gemm_nt(dt, R, d, Hq * dh, O, w->Wo, X, Z, s)) != hipSuccess) return hip_fail(e, "output projection");
+  dg::VocabPlan vp = dg::vocab_plan(R, d, dims->V, dt);
+  if ((e = dg::launch_vocab(vp, Z, w->E, io->max_logit, io->argmax, io->conf, io->lse, io->selfcond_out,
+                            scratch, s)) != hipSuccess)
+    return hip_fail(e, "vocab/self-conditioning");
+  if ((e = dg::launch_renoise(R, dims->C, dims->V, io->argmax, io->conf, tau, seed, t, block,
+                              io->tokens_out, io->mask, s)) != hipSuccess)
+    return hip_fail(e, "renoise");
+  return DG_OK;
+}
+
+int dg_prefill_append(const dg_dims* dims, const dg_weights* w, const void* H,
+                      const int32_t* tokens_final, void* k_cache, void* v_cache, void* attn_out,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int st = check_dims(dims, true);
+  if (st != DG_OK) return st;
+  if (!w || !w->Wq || !w->Wk || !w->Wv || !w->E || !H || !tokens_final || !k_cache || !v_cache)
+    return fail(DG_EINVAL, "weights (Wq, Wk, Wv, E), H, tokens_final and the caches must be non-NULL");
+  if (dims->L + dims->C > dims->cap)
+    return fail(DG_EINVAL, "append needs L + C <= cap (L=%d C=%d cap=%d)", dims->L, dims->C, dims->cap);
+  if (dims->dtype == DG_BF16 && dims->d % 64)
+    return fail(DG_EUNSUPPORTED, "bf16 append needs d %% 64 == 0");
+  const void* ptrs[] = {w->Wq, w->Wk, w->Wv, w->E, H, k_cache, v_cache, attn_out};
+  if ((st = check_bf16_align(dims, ptrs, 8)) != DG_OK) return st;
+  const StepLayout L = step_layout(dims);
+  if (!ws || ws_bytes < L.total)
+    return fail(DG_EWORKSPACE, "append workspace needs %zu bytes (got %zu)", L.total, ws ? ws_bytes : 0);
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = dims->dtype, d = dims->d, Hq = dims->n_q_heads, Hkv = dims->n_kv_heads, dh = dims->head_dim;
+  const int R = dims->B * dims->C;
+  void* X = at(ws, L.X);
+  void* Q = at(ws, L.Q);
+  void* Kn = at(ws, L.Kn);
+  void* Vn = at(ws, L.Vn);
+  void* O = attn_out ? attn_out : at(ws, L.O);
+  hipError_t e;
+  if ((e = dg::launch_assemble(dt, R, d, dims->V, H, w->E, tokens_final, nullptr, X, s)) != hipSuccess)
+    return hip_fail(e, "assemble");
+  if ((e = dg::launch_gemm_nt(dt, R, Hq * dh, d, X, w->Wq, nullptr, Q, s)) != hipSuccess) return hip_fail(e, "Q projection");
+  if ((e = dg::launch_gemm_nt(dt, R, Hkv * dh, d, X, w->Wk, nullptr, Kn, s)) != hipSuccess) return hip_fail(e, "K projection");
+  if ((e = dg::launch_gemm_nt(dt, R, Hkv * dh, d, X, w->Wv, nullptr, Vn, s)) != hipSuccess) return hip_fail(e, "V projection");
+  if ((e = dg::launch_cache_append(dt, dims->B, dims->C, dims->L, dims->cap, Hkv, dh, Kn, k_cache, s)) != hipSuccess)
+    return hip_fail(e, "K cache append");
+  if ((e = dg::launch_cache_append(dt, dims->B, dims->C, dims->L, dims->cap, Hkv, dh, Vn, v_cache, s)) != hipSuccess)
+    return hip_fail(e, "V cache append");
+  dg::AttnPlan ap = dg::attn_plan(dims->B, dims->C, dims->L, dims->cap, Hq, Hkv, dh, dt, 1);
+  if ((e = dg::launch_attn(ap, Q, k_cache, v_cache, Kn, Vn, O, nullptr, at(ws, L.scratch), s)) != hipSuccess)
+    return hip_fail(e, "causal attention");
+  return DG_OK;
+}
+
+}  // extern "C"

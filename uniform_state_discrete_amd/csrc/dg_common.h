@@ -1,0 +1,96 @@
+// Internal helpers shared by the gfx950 kernels of libdg (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace dg {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 8 bf16
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // 4 bf16
+
+#define DG_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+// bf16 value of the rounded float (used to keep sums consistent with the packed operand).
+__device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(f32_to_bf16(f) << 16); }
+
+// D = A.B + C on a 32x32x16 bf16 tile.  Lane l supplies A[m = l%32][k = 8(l/32)+i],
+// B[k = 8(l/32)+i][n = l%32] (i = 0..7); D lane l holds D[8j + 4(l/32) + i][l%32]
+// at element 4j + i.
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Transposing LDS read: within each 16-lane group, lane p points at 4
+// consecutive bf16 of row p/4 (cols 4(p%4)..+3) of a 4 x 16 block; lane p then
+// receives column p of that block (rows 0..3).
+__device__ __forceinline__ u32x2 lds_read_tr16(const DG_LDS u16* p) {
+  bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((DG_LDS bf16x4_t*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ u32x4 ldg128(const u16* p) { return *(const u32x4*)p; }
+
+}  // namespace dg
+
+// Launch wrappers (host side), implemented next to their kernels.  Each returns
+// the hipError_t of its launch.  Pointers and sizes are already validated.
+namespace dg {
+struct VocabPlan {
+  int rows, d, V, nrb, nsplit, split_len, variant;  // variant: 0 fp32 rowwise, 1 bf16 32-row, 2 bf16 16-row
+  size_t part_S_bytes, part_stat_bytes;
+};
+VocabPlan vocab_plan(int rows, int d, int V, int dtype);
+hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float* max_logit,
+                        int32_t* argmax, float* conf, float* lse, void* selfcond, void* ws,
+                        hipStream_t s);
+
+struct AttnPlan {
+  int B, C, L, cap, Hq, Hkv, dh, dtype, causal, nrb, nsplit, keys_per_split;
+  size_t part_bytes;
+};
+AttnPlan attn_plan(int B, int C, int L, int cap, int Hq, int Hkv, int dh, int dtype, int causal);
+hipError_t launch_attn(const AttnPlan& p, const void* q, const void* kc, const void* vc,
+                       const void* kn, const void* vn, void* out, float* lse, void* ws,
+                       hipStream_t s);
+
+// C[M][N] = A[M][K] . B[N][K]^T (+ Res[M][N]); dtype 0 fp32, 1 bf16.
+hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const void* B,
+                          const void* Res, void* C, hipStream_t s);
+
+hipError_t launch_assemble(int dtype, int R, int d, int V, const void* H, const void* E,
+                           const int32_t* x, const void* S, void* X, hipStream_t s);
+hipError_t launch_renoise(int rows, int canvas, int V, const int32_t* argmax, const float* conf,
+                          float tau, uint64_t seed, uint32_t t, uint32_t block, int32_t* out,
+                          uint8_t* mask, hipStream_t s);
+// Scatter canvas rows kn[B][C][Hkv][dh] into cache[B][Hkv][cap][dh] at rows [L, L+C).
+hipError_t launch_cache_append(int dtype, int B, int C, int L, int cap, int Hkv, int dh,
+                               const void* kn, void* cache, hipStream_t s);
+}  // namespace dg

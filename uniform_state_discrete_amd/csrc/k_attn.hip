@@ -1,0 +1,351 @@
+// Canvas attention over [KV cache || canvas] (DiffusionGemma explainer,
+// "Architettura: il prefill incrementale e il denoising"): bidirectional in
+// denoising (every canvas query sees every canvas token and the whole cache),
+// causal in the incremental prefill of a finished block (query i sees the
+// cache and canvas keys 0..i).
+#include "dg_common.h"
+#include <math.h>
+
+namespace dg {
+
+// ---------------------------------------------------------------------------
+// bf16 path.  One workgroup = one (canvas b, KV head g), 128 packed query rows
+// (row = canvas position * G + head-in-group: the G query heads sharing a KV
+// head share every K/V tile), and one split of the keys.  4 waves x 32 rows.
+//
+// Both products are computed transposed so that each lane owns one query row:
+//   S^T[key][row] = K . Q^T   (A = K tile from LDS, B = Q fragments in VGPRs)
+//   O^T[dh][row] += V^T . P^T (A = V tile read transposed from LDS with
+//                              ds_read_b64_tr_b16, B = P straight from S^T)
+// The key order inside a 16-deep MFMA step is permuted identically on both
+// operands, so P never leaves registers.  Online softmax in the log2 domain.
+// K/V tiles of 64 keys are double-buffered in LDS through registers; one
+// barrier per tile.  Rows of the K tile are padded by 16 B and of the V tile
+// by 64 B so that the row-wise and the transposing reads are conflict-free.
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ void __launch_bounds__(256, 2)
+    k_attn_bf16(int B, int C, int L, int cap, int Hq, int Hkv, int G, int causal, int nrb,
+                int nsplit, int kps, const u16* __restrict__ Q, const u16* __restrict__ Kc,
+                const u16* __restrict__ Vc, const u16* __restrict__ Kn, const u16* __restrict__ Vn,
+                u16* __restrict__ O, float* __restrict__ lse_out, float* __restrict__ Opart,
+                float* __restrict__ mpart, float* __restrict__ lpart) {
+  constexpr int KP = DH + 8, VP = DH + 32, KS = DH / 16, MB = DH / 32;
+  constexpr int CPR = DH / 8, NLD = 64 * CPR / 256;
+  __shared__ __attribute__((aligned(16))) u16 Ks[2][64][KP];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2][64][VP];
+
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, l32 = l & 31;
+  int bid = blockIdx.x;
+  const int rb = bid % nrb;
+  bid /= nrb;
+  const int split = bid % nsplit;
+  bid /= nsplit;
+  const int g = bid % Hkv, b = bid / Hkv;
+  const int nkeys = L + C;
+  const int k_begin = split * kps;
+  const int k_end = min(nkeys, k_begin + kps);
+  const int M = C * G;
+  const int row = rb * 128 + w * 32 + l32;
+  const bool rok = row < M;
+  const int qi = rok ? row / G : 0, qh = g * G + (rok ? row % G : 0);
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+  u32x4 qf[KS];
+  {
+    const u16* qp = Q + (((size_t)b * C + qi) * Hq + qh) * DH + h * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = rok ? ldg128(qp + ks * 16) : z4;
+  }
+  f32x16 oacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) oacc[mb] = zero16();
+  float m = -INFINITY, lsum = 0.f;
+  const float sl2 = kLog2e * rsqrtf((float)DH);
+  const int qlim = L + qi;  // causal: key <= L + i
+
+  u32x4 kreg[NLD], vreg[NLD];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = threadIdx.x + u * 256;
+      const int rr = idx / CPR, cc = (idx % CPR) * 8;
+      const int key = t0 + rr;
+      const bool ok = key < k_end;
+      size_t o;
+      const u16 *kp, *vp;
+      if (key < L) {
+        o = (((size_t)b * Hkv + g) * cap + key) * DH + cc;
+        kp = Kc + o;
+        vp = Vc + o;
+      } else {
+        o = (((size_t)b * C + (ok ? key - L : 0)) * Hkv + g) * DH + cc;
+        kp = Kn + o;
+        vp = Vn + o;
+      }
+      kreg[u] = ok ? ldg128(kp) : z4;
+      vreg[u] = ok ? ldg128(vp) : z4;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = threadIdx.x + u * 256;
+      const int rr = idx / CPR, cc = (idx % CPR) * 8;
+      *(u32x4*)&Ks[buf][rr][cc] = kreg[u];
+      *(u32x4*)&Vs[buf][rr][cc] = vreg[u];
+    }
+  };
+
+  const int ntiles = k_end > k_begin ? (k_end - k_begin + 63) / 64 : 0;
+  if (ntiles > 0) {
+    load_tile(k_begin);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int t0 = k_begin + t * 64;
+    if (t + 1 < ntiles) load_tile(t0 + 64);
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 ka = *(const u32x4*)&Ks[buf][kb * 32 + l32][ks * 16 + h * 8];
+        sacc[kb] = mfma32(ka, qf[ks], sacc[kb]);
+      }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = t0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+        const bool valid = key < k_end && (!causal || key <= qlim);
+        const float s = valid ? sacc[kb][e] * sl2 : -INFINITY;
+        sacc[kb][e] = s;
+        tmax = fmaxf(tmax, s);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(m, tmax);
+    if (mnew > m) {
+      const float alpha = exp2f(m - mnew);  // m = -inf gives 0
+      lsum *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+      m = mnew;
+    }
+    u32x4 pf[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float s = sacc[q >> 1][8 * (q & 1) + e];
+        pv[e] = (s == -INFINITY) ? 0.f : round_bf16(exp2f(s - m));
+        lsum += pv[e];
+      }
+      pf[q] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                    pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+    }
+    const DG_LDS u16* vbase = (const DG_LDS u16*)&Vs[buf][0][0];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r0 = 16 * q + 4 * h + ((l & 15) >> 2);
+        const int c0 = mb * 32 + 16 * ((l >> 4) & 1) + (l & 3) * 4;
+        const u32x2 a0 = lds_read_tr16(vbase + r0 * VP + c0);
+        const u32x2 a1 = lds_read_tr16(vbase + (r0 + 8) * VP + c0);
+        oacc[mb] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf[q], oacc[mb]);
+      }
+    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  lsum += __shfl_xor(lsum, 32);
+  if (!rok) return;
+  const size_t orow = ((size_t)b * C + qi) * Hq + qh;
+  if (nsplit == 1) {
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int f = mb * 32 + 8 * j + 4 * h;
+        u32x2 o2 = {pack_bf16x2(oacc[mb][4 * j] * inv, oacc[mb][4 * j + 1] * inv),
+                    pack_bf16x2(oacc[mb][4 * j + 2] * inv, oacc[mb][4 * j + 3] * inv)};
+        *(u32x2*)(O + orow * DH + f) = o2;
+      }
+    if (lse_out && h == 0) lse_out[orow] = (m + log2f(lsum)) * kLn2;
+  } else {
+    const size_t nrows = (size_t)B * C * Hq;
+    float* op = Opart + ((size_t)split * nrows + orow) * DH;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int f = mb * 32 + 8 * j + 4 * h;
+        *(f32x4*)(op + f) = f32x4{oacc[mb][4 * j], oacc[mb][4 * j + 1], oacc[mb][4 * j + 2],
+                                  oacc[mb][4 * j + 3]};
+      }
+    if (h == 0) {
+      mpart[split * nrows + orow] = m;
+      lpart[split * nrows + orow] = lsum;
+    }
+  }
+}
+
+// Merge of the key splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// splits in a fixed order (deterministic).  One workgroup per (b, i, h) row.
+__global__ void k_attn_combine_bf16(int nrows, int nsplit, int dh, const float* __restrict__ Opart,
+                                    const float* __restrict__ mpart, const float* __restrict__ lpart,
+                                    u16* __restrict__ O, float* __restrict__ lse_out) {
+  const int r = blockIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, mpart[(size_t)s * nrows + r]);
+  float Lt = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = mpart[(size_t)s * nrows + r];
+    if (ms != -INFINITY) Lt += exp2f(ms - M) * lpart[(size_t)s * nrows + r];
+  }
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+  for (int f = threadIdx.x; f < dh; f += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = mpart[(size_t)s * nrows + r];
+      if (ms != -INFINITY) acc += exp2f(ms - M) * Opart[((size_t)s * nrows + r) * dh + f];
+    }
+    O[(size_t)r * dh + f] = (u16)f32_to_bf16(acc * inv);
+  }
+  if (lse_out && threadIdx.x == 0) lse_out[r] = (M + log2f(Lt)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: one workgroup per (b, i, h) query row, keys in chunks of 256 (one
+// per lane), exact online softmax with expf/logf, lane f < dh accumulates
+// output feature f.  For the small fp32 workloads.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_attn_f32(int B, int C, int L, int cap, int Hq, int Hkv,
+                                                  int G, int dh, int causal,
+                                                  const float* __restrict__ Q,
+                                                  const float* __restrict__ Kc,
+                                                  const float* __restrict__ Vc,
+                                                  const float* __restrict__ Kn,
+                                                  const float* __restrict__ Vn,
+                                                  float* __restrict__ O, float* __restrict__ lse_out) {
+  __shared__ float qs[256], ps[256], red[256];
+  const int r = blockIdx.x;
+  const int hq = r % Hq, i = (r / Hq) % C, b = r / (Hq * C);
+  const int g = hq / G;
+  const int tid = threadIdx.x;
+  if (tid < dh) qs[tid] = Q[(size_t)r * dh + tid];
+  __syncthreads();
+  const float scale = 1.0f / sqrtf((float)dh);
+  const int nkeys = L + C;
+  float m = -INFINITY, lsum = 0.f, oacc = 0.f;
+  for (int j0 = 0; j0 < nkeys; j0 += 256) {
+    const int j = j0 + tid;
+    float s = -INFINITY;
+    if (j < nkeys && (!causal || j <= L + i)) {
+      const float* kp = j < L ? Kc + (((size_t)b * Hkv + g) * cap + j) * dh
+                              : Kn + (((size_t)b * C + (j - L)) * Hkv + g) * dh;
+      float acc = 0.f;
+      for (int f = 0; f < dh; ++f) acc = fmaf(qs[f], kp[f], acc);
+      s = acc * scale;
+    }
+    red[tid] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+      __syncthreads();
+    }
+    const float mnew = fmaxf(m, red[0]);
+    __syncthreads();
+    const float alpha = (mnew == -INFINITY) ? 1.f : expf(m - mnew);
+    const float p = (s == -INFINITY) ? 0.f : expf(s - mnew);
+    ps[tid] = p;
+    red[tid] = p;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (tid < o) red[tid] += red[tid + o];
+      __syncthreads();
+    }
+    lsum = lsum * alpha + red[0];
+    m = mnew;
+    if (tid < dh) {
+      float acc = oacc * alpha;
+      const int jn = min(256, nkeys - j0);
+      for (int jj = 0; jj < jn; ++jj) {
+        const int jk = j0 + jj;
+        const float* vp = jk < L ? Vc + (((size_t)b * Hkv + g) * cap + jk) * dh
+                                 : Vn + (((size_t)b * C + (jk - L)) * Hkv + g) * dh;
+        acc = fmaf(ps[jj], vp[tid], acc);
+      }
+      oacc = acc;
+    }
+    __syncthreads();
+  }
+  if (tid < dh) O[(size_t)r * dh + tid] = oacc / lsum;
+  if (lse_out && tid == 0) lse_out[r] = m + logf(lsum);
+}
+
+// ---------------------------------------------------------------------------
+AttnPlan attn_plan(int B, int C, int L, int cap, int Hq, int Hkv, int dh, int dtype, int causal) {
+  AttnPlan p{};
+  p.B = B; p.C = C; p.L = L; p.cap = cap; p.Hq = Hq; p.Hkv = Hkv; p.dh = dh; p.dtype = dtype;
+  p.causal = causal;
+  const int nkeys = L + C;
+  if (dtype == 1) {
+    const int G = Hq / Hkv;
+    p.nrb = (C * G + 127) / 128;
+    const int pairs = B * Hkv * p.nrb;
+    int ns = (512 + pairs - 1) / pairs;             // about two workgroups per CU
+    const int maxs = (nkeys + 127) / 128;           // at least two 64-key tiles per split
+    ns = ns < 1 ? 1 : (ns > maxs ? maxs : ns);
+    p.keys_per_split = ((nkeys + ns - 1) / ns + 63) / 64 * 64;
+    p.nsplit = (nkeys + p.keys_per_split - 1) / p.keys_per_split;
+    if (p.nsplit < 1) p.nsplit = 1;
+    p.part_bytes = p.nsplit > 1 ? (size_t)p.nsplit * B * C * Hq * (dh + 2) * sizeof(float) : 0;
+  } else {
+    p.nrb = 1; p.nsplit = 1; p.keys_per_split = nkeys; p.part_bytes = 0;
+  }
+  return p;
+}
+
+hipError_t launch_attn(const AttnPlan& p, const void* q, const void* kc, const void* vc,
+                       const void* kn, const void* vn, void* out, float* lse, void* ws,
+                       hipStream_t s) {
+  const int G = p.Hq / p.Hkv;
+  const size_t nrows = (size_t)p.B * p.C * p.Hq;
+  if (nrows == 0) return hipSuccess;
+  if (p.dtype != 1) {
+    hipLaunchKernelGGL(k_attn_f32, dim3((unsigned)nrows), dim3(256), 0, s, p.B, p.C, p.L, p.cap,
+                       p.Hq, p.Hkv, G, p.dh, p.causal, (const float*)q, (const float*)kc,
+                       (const float*)vc, (const float*)kn, (const float*)vn, (float*)out, lse);
+    return hipGetLastError();
+  }
+  float* Opart = (float*)ws;
+  float* mpart = Opart + (size_t)p.nsplit * nrows * p.dh;
+  float* lpart = mpart + (size_t)p.nsplit * nrows;
+  const dim3 grid((unsigned)(p.nrb * p.nsplit * p.Hkv * p.B));
+#define DG_ATTN_LAUNCH(DHV)                                                                       \
+  hipLaunchKernelGGL(k_attn_bf16<DHV>, grid, dim3(256), 0, s, p.B, p.C, p.L, p.cap, p.Hq, p.Hkv, \
+                     G, p.causal, p.nrb, p.nsplit, p.keys_per_split, (const u16*)q,                \
+                     (const u16*)kc, (const u16*)vc, (const u16*)kn, (const u16*)vn, (u16*)out,    \
+                     lse, Opart, mpart, lpart)
+  if (p.dh == 128)
+    DG_ATTN_LAUNCH(128);
+  else
+    DG_ATTN_LAUNCH(64);
+#undef DG_ATTN_LAUNCH
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  hipLaunchKernelGGL(k_attn_combine_bf16, dim3((unsigned)nrows), dim3(128), 0, s, (int)nrows,
+                     p.nsplit, p.dh, Opart, mpart, lpart, (u16*)out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace dg

@@ -1,0 +1,161 @@
+// Small kernels of the denoise step: assemble X = H + E[x] + S, uniform-state
+// renoise with Philox4x64-10, and the cache append of a finished block.
+#include "dg_common.h"
+
+namespace dg {
+
+// ---------------------------------------------------------------------------
+// Assemble: X[r] = H[r] + E[x_r] + S[r] (S may be NULL).  The denoiser reads
+// the canvas tokens' embeddings on top of the hidden rows plus the
+// self-conditioning vector handed over from the previous step
+// (DiffusionGemma explainer, "Autocondizionamento").  Sum in fp32, one
+// rounding to the storage type.  One workgroup per row; 8 elements per lane.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_assemble_bf16(int d, int V, const u16* __restrict__ H,
+                                                       const u16* __restrict__ E,
+                                                       const int32_t* __restrict__ x,
+                                                       const u16* __restrict__ S,
+                                                       u16* __restrict__ X) {
+  const int r = blockIdx.x;
+  int tok = x[r];
+  if (tok < 0 || tok >= V) tok = 0;
+  const size_t ro = (size_t)r * d;
+  const size_t eo = (size_t)tok * d;
+  for (int e = threadIdx.x * 8; e < d; e += 256 * 8) {
+    u32x4 h = ldg128(H + ro + e);
+    u32x4 em = ldg128(E + eo + e);
+    u32x4 s = {0u, 0u, 0u, 0u};
+    if (S) s = ldg128(S + ro + e);
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float lo = bf16_to_f32(h[k] & 0xFFFFu) + bf16_to_f32(em[k] & 0xFFFFu) + bf16_to_f32(s[k] & 0xFFFFu);
+      float hi = bf16_to_f32(h[k] >> 16) + bf16_to_f32(em[k] >> 16) + bf16_to_f32(s[k] >> 16);
+      o[k] = pack_bf16x2(lo, hi);
+    }
+    *(u32x4*)(X + ro + e) = o;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_assemble_f32(int d, int V, const float* __restrict__ H,
+                                                      const float* __restrict__ E,
+                                                      const int32_t* __restrict__ x,
+                                                      const float* __restrict__ S,
+                                                      float* __restrict__ X) {
+  const int r = blockIdx.x;
+  int tok = x[r];
+  if (tok < 0 || tok >= V) tok = 0;
+  const size_t ro = (size_t)r * d;
+  const size_t eo = (size_t)tok * d;
+  for (int e = threadIdx.x; e < d; e += 256) {
+    float v = H[ro + e] + E[eo + e];
+    if (S) v += S[ro + e];
+    X[ro + e] = v;
+  }
+}
+
+hipError_t launch_assemble(int dtype, int R, int d, int V, const void* H, const void* E,
+                           const int32_t* x, const void* S, void* X, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_assemble_bf16, dim3(R), dim3(256), 0, s, d, V, (const u16*)H,
+                       (const u16*)E, x, (const u16*)S, (u16*)X);
+  else
+    hipLaunchKernelGGL(k_assemble_f32, dim3(R), dim3(256), 0, s, d, V, (const float*)H,
+                       (const float*)E, x, (const float*)S, (float*)X);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x64-10 (Salmon et al., SC'11, "Parallel random numbers: as easy as
+// 1, 2, 3"): 10 rounds of two 64x64->128 multiplies with the round constants
+// below, the key bumped by the Weyl constants between rounds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t philox_w0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                              uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += W0; k1 += W1; }
+    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+  }
+  return c0;
+}
+
+// Uniform-state renoise (explainer, "Diffusione dello stato uniforme"): a
+// position whose confidence is below tau gets a fresh uniform vocabulary
+// token; the others take the argmax.  conf == NULL draws every position
+// (a block's initial canvas).  Token = floor(w0 * V / 2^64).
+__global__ void k_renoise(int rows, int canvas, int V, const int32_t* __restrict__ argmax,
+                          const float* __restrict__ conf, float tau, uint64_t seed, uint32_t t,
+                          uint32_t block, int32_t* __restrict__ out, uint8_t* __restrict__ mask) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  const bool draw = (conf == nullptr) || (conf[r] < tau);
+  int tok;
+  if (draw) {
+    const uint32_t b = (uint32_t)(r / canvas), i = (uint32_t)(r % canvas);
+    const uint64_t w0 = philox_w0(i, t, b, block, seed, 0);
+    tok = (int)__umul64hi(w0, (uint64_t)V);
+  } else {
+    tok = argmax[r];
+  }
+  out[r] = tok;
+  if (mask) mask[r] = draw ? 1 : 0;
+}
+
+hipError_t launch_renoise(int rows, int canvas, int V, const int32_t* argmax, const float* conf,
+                          float tau, uint64_t seed, uint32_t t, uint32_t block, int32_t* out,
+                          uint8_t* mask, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_renoise, dim3((rows + 255) / 256), dim3(256), 0, s, rows, canvas, V,
+                     argmax, conf, tau, seed, t, block, out, mask);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Cache append: canvas rows kn[b][i][g][:] -> cache[b][g][L + i][:].
+// One 16-byte (bf16) or 4-byte (fp32) element group per lane.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void k_cache_append(int B, int C, int L, int cap, int Hkv, int dh, const T* __restrict__ kn,
+                               T* __restrict__ cache, int vec) {
+  const size_t n = (size_t)B * C * Hkv * dh / vec;
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+    const size_t el = e * vec;
+    const int f = (int)(el % dh);
+    const size_t rest = el / dh;
+    const int g = (int)(rest % Hkv);
+    const size_t bi = rest / Hkv;
+    const int i = (int)(bi % C), b = (int)(bi / C);
+    T* dst = cache + (((size_t)b * Hkv + g) * cap + L + i) * dh + f;
+    if (vec == 8) {
+      *(u32x4*)dst = *(const u32x4*)(kn + el);
+    } else {
+      *dst = kn[el];
+    }
+  }
+}
+
+hipError_t launch_cache_append(int dtype, int B, int C, int L, int cap, int Hkv, int dh,
+                               const void* kn, void* cache, hipStream_t s) {
+  const size_t n = (size_t)B * C * Hkv * dh;
+  if (n == 0) return hipSuccess;
+  if (dtype == 1) {
+    const size_t nv = n / 8;
+    const int grid = (int)((nv + 255) / 256 < 4096 ? (nv + 255) / 256 : 4096);
+    hipLaunchKernelGGL(k_cache_append<u16>, dim3(grid), dim3(256), 0, s, B, C, L, cap, Hkv, dh,
+                       (const u16*)kn, (u16*)cache, 8);
+  } else {
+    const int grid = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    hipLaunchKernelGGL(k_cache_append<float>, dim3(grid), dim3(256), 0, s, B, C, L, cap, Hkv, dh,
+                       (const float*)kn, (float*)cache, 1);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dg
