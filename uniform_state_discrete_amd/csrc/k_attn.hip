@@ -224,9 +224,10 @@ __global__ void k_attn_combine_bf16(int nrows, int nsplit, int dh, const float* 
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path: one workgroup per (b, i, h) query row, keys in chunks of 256 (one
-// per lane), exact online softmax with expf/logf, lane f < dh accumulates
-// output feature f.  For the small fp32 workloads.
+// fp32-storage path: one workgroup per (b, i, h) query row, keys in chunks of
+// 256 (one per lane), online softmax in fp64 (exp/log in double), lane f < dh
+// accumulates output feature f in fp64; only the stored O is rounded.  For
+// the small fp32 workloads.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) k_attn_f32(int B, int C, int L, int cap, int Hq, int Hkv,
                                                   int G, int dh, int causal,
@@ -236,36 +237,36 @@ __global__ void __launch_bounds__(256) k_attn_f32(int B, int C, int L, int cap, 
                                                   const float* __restrict__ Kn,
                                                   const float* __restrict__ Vn,
                                                   float* __restrict__ O, float* __restrict__ lse_out) {
-  __shared__ float qs[256], ps[256], red[256];
+  __shared__ double qs[256], ps[256], red[256];
   const int r = blockIdx.x;
   const int hq = r % Hq, i = (r / Hq) % C, b = r / (Hq * C);
   const int g = hq / G;
   const int tid = threadIdx.x;
-  if (tid < dh) qs[tid] = Q[(size_t)r * dh + tid];
+  if (tid < dh) qs[tid] = (double)Q[(size_t)r * dh + tid];
   __syncthreads();
-  const float scale = 1.0f / sqrtf((float)dh);
+  const double scale = 1.0 / sqrt((double)dh);
   const int nkeys = L + C;
-  float m = -INFINITY, lsum = 0.f, oacc = 0.f;
+  double m = -INFINITY, lsum = 0.0, oacc = 0.0;
   for (int j0 = 0; j0 < nkeys; j0 += 256) {
     const int j = j0 + tid;
-    float s = -INFINITY;
+    double s = -INFINITY;
     if (j < nkeys && (!causal || j <= L + i)) {
       const float* kp = j < L ? Kc + (((size_t)b * Hkv + g) * cap + j) * dh
                               : Kn + (((size_t)b * C + (j - L)) * Hkv + g) * dh;
-      float acc = 0.f;
-      for (int f = 0; f < dh; ++f) acc = fmaf(qs[f], kp[f], acc);
+      double acc = 0.0;
+      for (int f = 0; f < dh; ++f) acc = fma(qs[f], (double)kp[f], acc);
       s = acc * scale;
     }
     red[tid] = s;
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
-      if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+      if (tid < o) red[tid] = fmax(red[tid], red[tid + o]);
       __syncthreads();
     }
-    const float mnew = fmaxf(m, red[0]);
+    const double mnew = fmax(m, red[0]);
     __syncthreads();
-    const float alpha = (mnew == -INFINITY) ? 1.f : expf(m - mnew);
-    const float p = (s == -INFINITY) ? 0.f : expf(s - mnew);
+    const double alpha = (mnew == -INFINITY) ? 1.0 : exp(m - mnew);
+    const double p = (s == -INFINITY) ? 0.0 : exp(s - mnew);
     ps[tid] = p;
     red[tid] = p;
     __syncthreads();
@@ -276,20 +277,20 @@ __global__ void __launch_bounds__(256) k_attn_f32(int B, int C, int L, int cap, 
     lsum = lsum * alpha + red[0];
     m = mnew;
     if (tid < dh) {
-      float acc = oacc * alpha;
+      double acc = oacc * alpha;
       const int jn = min(256, nkeys - j0);
       for (int jj = 0; jj < jn; ++jj) {
         const int jk = j0 + jj;
         const float* vp = jk < L ? Vc + (((size_t)b * Hkv + g) * cap + jk) * dh
                                  : Vn + (((size_t)b * C + (jk - L)) * Hkv + g) * dh;
-        acc = fmaf(ps[jj], vp[tid], acc);
+        acc = fma(ps[jj], (double)vp[tid], acc);
       }
       oacc = acc;
     }
     __syncthreads();
   }
-  if (tid < dh) O[(size_t)r * dh + tid] = oacc / lsum;
-  if (lse_out && tid == 0) lse_out[r] = m + logf(lsum);
+  if (tid < dh) O[(size_t)r * dh + tid] = (float)(oacc / lsum);
+  if (lse_out && tid == 0) lse_out[r] = (float)(m + log(lsum));
 }
 
 // ---------------------------------------------------------------------------

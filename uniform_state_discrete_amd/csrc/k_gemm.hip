@@ -79,7 +79,8 @@ __global__ void __launch_bounds__(256) k_gemm_nt_bf16(int M, int N, int K, const
   }
 }
 
-// fp32 path: classic 16x16 LDS-tiled GEMM, fp32 FMA, sequential over K.
+// fp32-storage path: classic 16x16 LDS-tiled GEMM accumulating in fp64 (one
+// rounding of the stored output), sequential over K.
 __global__ void __launch_bounds__(256) k_gemm_nt_f32(int M, int N, int K, const float* __restrict__ A,
                                                      const float* __restrict__ B,
                                                      const float* __restrict__ Res,
@@ -87,7 +88,7 @@ __global__ void __launch_bounds__(256) k_gemm_nt_f32(int M, int N, int K, const 
   __shared__ float As[16][17], Bs[16][17];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int m = blockIdx.y * 16 + ty, n = blockIdx.x * 16 + tx;
-  float acc = 0.f;
+  double acc = 0.0;
   for (int k0 = 0; k0 < K; k0 += 16) {
     const int ka = k0 + tx;
     As[ty][tx] = (m < M && ka < K) ? A[(size_t)m * K + ka] : 0.f;
@@ -95,12 +96,12 @@ __global__ void __launch_bounds__(256) k_gemm_nt_f32(int M, int N, int K, const 
     Bs[ty][tx] = (nb < N && ka < K) ? B[(size_t)nb * K + ka] : 0.f;
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) acc = fmaf(As[ty][kk], Bs[tx][kk], acc);
+    for (int kk = 0; kk < 16; ++kk) acc = fma((double)As[ty][kk], (double)Bs[tx][kk], acc);
     __syncthreads();
   }
   if (m < M && n < N) {
-    if (Res) acc += Res[(size_t)m * N + n];
-    C[(size_t)m * N + n] = acc;
+    if (Res) acc += (double)Res[(size_t)m * N + n];
+    C[(size_t)m * N + n] = (float)acc;
   }
 }
 

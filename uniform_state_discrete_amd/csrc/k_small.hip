@@ -8,8 +8,8 @@ namespace dg {
 // Assemble: X[r] = H[r] + E[x_r] + S[r] (S may be NULL).  The denoiser reads
 // the canvas tokens' embeddings on top of the hidden rows plus the
 // self-conditioning vector handed over from the previous step
-// (DiffusionGemma explainer, "Autocondizionamento").  Sum in fp32, one
-// rounding to the storage type.  One workgroup per row; 8 elements per lane.
+// (DiffusionGemma explainer, "Autocondizionamento").  One rounding to the
+// storage type (bf16: fp32 sum; fp32: fp64 sum).  One workgroup per row.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) k_assemble_bf16(int d, int V, const u16* __restrict__ H,
                                                        const u16* __restrict__ E,
@@ -48,9 +48,9 @@ __global__ void __launch_bounds__(256) k_assemble_f32(int d, int V, const float*
   const size_t ro = (size_t)r * d;
   const size_t eo = (size_t)tok * d;
   for (int e = threadIdx.x; e < d; e += 256) {
-    float v = H[ro + e] + E[eo + e];
-    if (S) v += S[ro + e];
-    X[ro + e] = v;
+    double v = (double)H[ro + e] + (double)E[eo + e];
+    if (S) v += (double)S[ro + e];
+    X[ro + e] = (float)v;
   }
 }
 

@@ -480,8 +480,9 @@ __global__ void __launch_bounds__(256) k_vocab_combine(int R, int d, int nsplit,
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path: one workgroup per row, vocab ids in chunks of 256 (one per lane),
-// exact online softmax with expf; lane k accumulates S columns k, k+256, ...
+// fp32-storage path: one workgroup per row, vocab ids in chunks of 256 (one
+// per lane), online softmax in fp64 (exp/log in double), lane k accumulates S
+// columns k, k+256, ... in fp64; only the stored outputs are rounded.
 // ---------------------------------------------------------------------------
 constexpr int kF32MaxD = 4096;
 __global__ void __launch_bounds__(256) k_vocab_f32(int R, int d, int V, const float* __restrict__ Z,
@@ -491,23 +492,23 @@ __global__ void __launch_bounds__(256) k_vocab_f32(int R, int d, int V, const fl
                                                    float* __restrict__ conf, float* __restrict__ lse,
                                                    float* __restrict__ S) {
   __shared__ float zs[kF32MaxD];
-  __shared__ float ps[256], rv[256];
+  __shared__ double ps[256], rv[256];
   __shared__ int ri[256];
   const int r = blockIdx.x, tid = threadIdx.x;
   for (int e = tid; e < d; e += 256) zs[e] = Z[(size_t)r * d + e];
   __syncthreads();
-  float sacc[kF32MaxD / 256];
+  double sacc[kF32MaxD / 256];
 #pragma unroll
-  for (int k = 0; k < kF32MaxD / 256; ++k) sacc[k] = 0.f;
-  float m = -INFINITY, lsum = 0.f;
+  for (int k = 0; k < kF32MaxD / 256; ++k) sacc[k] = 0.0;
+  double m = -INFINITY, lsum = 0.0;
   int am = 0;
   for (int v0 = 0; v0 < V; v0 += 256) {
     const int v = v0 + tid;
-    float lgv = -INFINITY;
+    double lgv = -INFINITY;
     if (v < V) {
       const float* er = E + (size_t)v * d;
-      float a = 0.f;
-      for (int e = 0; e < d; ++e) a = fmaf(zs[e], er[e], a);
+      double a = 0.0;
+      for (int e = 0; e < d; ++e) a = fma((double)zs[e], (double)er[e], a);
       lgv = a;
     }
     rv[tid] = lgv;
@@ -515,19 +516,19 @@ __global__ void __launch_bounds__(256) k_vocab_f32(int R, int d, int V, const fl
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
       if (tid < o) {
-        const float x = rv[tid + o];
+        const double x = rv[tid + o];
         const int xi = ri[tid + o];
         if (x > rv[tid] || (x == rv[tid] && xi < ri[tid])) { rv[tid] = x; ri[tid] = xi; }
       }
       __syncthreads();
     }
-    const float cm = rv[0];
+    const double cm = rv[0];
     const int ca = ri[0];
     __syncthreads();
-    float mnew = m;
+    double mnew = m;
     if (cm > m) { mnew = cm; am = ca; }
-    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mnew);
-    const float p = v < V ? expf(lgv - mnew) : 0.f;
+    const double alpha = (m == -INFINITY) ? 0.0 : exp(m - mnew);
+    const double p = v < V ? exp(lgv - mnew) : 0.0;
     ps[tid] = p;
     rv[tid] = p;
     __syncthreads();
@@ -542,8 +543,8 @@ __global__ void __launch_bounds__(256) k_vocab_f32(int R, int d, int V, const fl
     for (int k = 0; k < kF32MaxD / 256; ++k) {
       const int e = tid + 256 * k;
       if (e < d) {
-        float a = sacc[k] * alpha;
-        for (int jj = 0; jj < vn; ++jj) a = fmaf(ps[jj], E[(size_t)(v0 + jj) * d + e], a);
+        double a = sacc[k] * alpha;
+        for (int jj = 0; jj < vn; ++jj) a = fma(ps[jj], (double)E[(size_t)(v0 + jj) * d + e], a);
         sacc[k] = a;
       }
     }
@@ -552,13 +553,13 @@ __global__ void __launch_bounds__(256) k_vocab_f32(int R, int d, int V, const fl
 #pragma unroll
   for (int k = 0; k < kF32MaxD / 256; ++k) {
     const int e = tid + 256 * k;
-    if (e < d) S[(size_t)r * d + e] = sacc[k] / lsum;
+    if (e < d) S[(size_t)r * d + e] = (float)(sacc[k] / lsum);
   }
   if (tid == 0) {
-    max_logit[r] = m;
+    max_logit[r] = (float)m;
     argmax[r] = am;
-    conf[r] = 1.f / lsum;
-    if (lse) lse[r] = m + logf(lsum);
+    conf[r] = (float)(1.0 / lsum);
+    if (lse) lse[r] = (float)(m + log(lsum));
   }
 }
 
