@@ -1,0 +1,244 @@
+"""Benchmark of the canvas denoise step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--copy-mib M]
+
+A step is one dg_denoise_step over the whole canvas (assemble, projections,
+bidirectional canvas attention over the KV cache, output projection, fused
+vocabulary head / confidence / self-conditioning, renoise), chained: step s
+consumes step s-1's tokens and self-conditioning vector.  Inputs are seeded
+synthetic tensors already resident in HBM.  Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+DEFAULT_WORKLOAD = "canvas256_L8192_d2048_V262144"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_vocab_traffic.json")
+VOCAB_SOURCES = [os.path.join(ROOT, "uniform_state_discrete_amd", "csrc", f)
+                 for f in ("k_vocab.hip", "dg_common.h")]
+
+
+def vocab_source_hash():
+    h = hashlib.sha256()
+    for p in VOCAB_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def algorithmic(cfg):
+    """Per-step algorithmic work (what the method must compute / move)."""
+    R = cfg.B * cfg.C
+    fl_vocab = 4.0 * R * cfg.V * cfg.d                       # logits + P.E
+    fl_attn = 4.0 * R * (cfg.L + cfg.C) * cfg.Hq * cfg.dh    # QK^T + PV
+    fl_proj = 2.0 * R * cfg.d * (cfg.Hq + 2 * cfg.Hkv) * cfg.dh + 2.0 * R * cfg.Hq * cfg.dh * cfg.d
+    by_E = cfg.V * cfg.d * 2.0
+    by_cache = 2.0 * cfg.B * cfg.L * cfg.Hkv * cfg.dh * 2.0
+    by_w = (2 * cfg.Hq + 2 * cfg.Hkv) * cfg.dh * cfg.d * 2.0
+    return dict(fl_vocab=fl_vocab, fl_attn=fl_attn, fl_proj=fl_proj, flops=fl_vocab + fl_attn + fl_proj,
+                by_E=by_E, by_cache=by_cache, bytes=by_E + by_cache + by_w)
+
+
+def read_traffic():
+    """HBM bytes per flash-vocab launch from the committed rocprofv3 counter
+    runs, or None when they were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != vocab_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(p, cfg, rows=8):
+    """The oracle, as it stands, on a bounded sample of the same step: the
+    assemble and K/V projections for every canvas row (the keys need them) and
+    Q, attention, Z, vocabulary head, self-conditioning and renoise for `rows`
+    rows; the per-row part is scaled to the full canvas."""
+    import numpy as np
+    from oracle import numerics, philox, step
+    from synth import from_storage
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    f = lambda a: from_storage(a, cfg.dtype).astype(np.float64)
+    E, H, Kc, Vc = f(p.E), f(p.H[0]), f(p.Kc), f(p.Vc)
+    W = {k: f(v) for k, v in p.W.items()}
+    R = cfg.B * cfg.C
+    x = step.init_canvas(cfg.seed, 0, cfg.B, cfg.C, cfg.V)
+    t0 = time.perf_counter()
+    X = step.assemble(H, E, x, None, cfg.dtype).reshape(R, cfg.d)
+    Kn = step.linear(X, W["Wk"], cfg.dtype).reshape(cfg.B, cfg.C, cfg.Hkv, cfg.dh)
+    Vn = step.linear(X, W["Wv"], cfg.dtype).reshape(cfg.B, cfg.C, cfg.Hkv, cfg.dh)
+    t1 = time.perf_counter()
+    sel = np.arange(rows) * (R // rows)
+    Q = step.linear(X[sel], W["Wq"], cfg.dtype).reshape(rows, cfg.Hq, cfg.dh)
+    O = np.empty((rows, cfg.Hq * cfg.dh))
+    for n, r in enumerate(sel):
+        b, i = divmod(int(r), cfg.C)
+        for h in range(cfg.Hq):
+            o, _ = step.attention_row(Q[n, h], b, h // cfg.G, i, Kc, Vc, Kn, Vn, cfg.L, False)
+            O[n, h * cfg.dh:(h + 1) * cfg.dh] = o
+    Z = numerics.round_store(X[sel] + numerics.round_store(O, cfg.dtype) @ W["Wo"].T, cfg.dtype)
+    m, a, lse, c, S, _ = step.vocab_rows(Z, E)
+    for n, r in enumerate(sel):
+        if c[n] < np.float32(cfg.tau[0]):
+            philox.uniform_token(cfg.seed, 1, int(r) // cfg.C, 0, int(r) % cfg.C, cfg.V)
+    t2 = time.perf_counter()
+    per_step = (t1 - t0) + (t2 - t1) * (R / rows)
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"numpy fp64 oracle, one step of {cfg.name}: assemble + K/V projections for all "
+                      f"{R} rows ({t1 - t0:.2f} s) + Q/attention/Z/vocab/self-conditioning/renoise for "
+                      f"{rows} rows ({t2 - t1:.2f} s) scaled x{R // rows}; est. {per_step:.1f} s/step"}
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size, for scaling HBM counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0, help="only run a plain copy of this size")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_mib:
+        copy_calibration(args.copy_mib)
+        return
+
+    import numpy as np
+    import torch
+
+    import uniform_state_discrete_amd as dg
+    from synth import config_by_name, gen_problem, tau_schedule
+
+    cfg = config_by_name(args.workload)
+    torch.cuda.set_device(0)
+    p = gen_problem(cfg)
+    W = {k: dg.to_device(v) for k, v in p.W.items()}
+    W["E"] = dg.to_device(p.E)
+    Kc, Vc, H = dg.to_device(p.Kc), dg.to_device(p.Vc), dg.to_device(p.H[0])
+    fdt = W["E"].dtype
+    code = dg.DG_BF16 if cfg.dtype == "bf16" else dg.DG_F32
+    dims = dg.make_dims(cfg.B, cfg.C, cfg.L, cfg.cap, cfg.d, cfg.Hq, cfg.Hkv, cfg.dh, cfg.V, code)
+    ws = dg.workspace(dg.dg_workspace_bytes(dims))
+    R = cfg.R
+    tok = [torch.empty((cfg.B, cfg.C), dtype=torch.int32, device="cuda") for _ in range(2)]
+    sc = [torch.zeros((cfg.B, cfg.C, cfg.d), dtype=fdt, device="cuda") for _ in range(2)]
+    stats = dict(max_logit=torch.empty(R, device="cuda"), conf=torch.empty(R, device="cuda"),
+                 lse=torch.empty(R, device="cuda"), argmax=torch.empty(R, dtype=torch.int32, device="cuda"),
+                 mask=torch.empty(R, dtype=torch.uint8, device="cuda"))
+    taus = tau_schedule(cfg)
+    stream = torch.cuda.current_stream()
+    dg.dg_init_canvas(R, cfg.C, cfg.V, cfg.seed, 0, tok[0])
+
+    def mk_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)       # materialise the HIP event
+        return evs
+
+    K = args.steps
+    ev = {k: mk_events(K) for k in ("vb", "ve", "ab", "ae")}
+    kept = []
+
+    def run(s, timed_index=None):
+        a, b = s % 2, (s + 1) % 2
+        io = dict(H=H, k_cache=Kc, v_cache=Vc, tokens_in=tok[a], selfcond_in=None if s == 0 else sc[a],
+                  tokens_out=tok[b], selfcond_out=sc[b], **stats)
+        if timed_index is not None:
+            io.update(ev_vocab_begin=ev["vb"][timed_index], ev_vocab_end=ev["ve"][timed_index],
+                      ev_attn_begin=ev["ab"][timed_index], ev_attn_end=ev["ae"][timed_index])
+        dg.dg_denoise_step(dims, W, io, taus[s % cfg.steps], cfg.seed, s % cfg.steps + 1, 0, ws, stream)
+
+    for s in range(args.warmup):
+        run(s)
+    torch.cuda.synchronize()
+    kept.append(1.0 - float(stats["mask"].float().mean()))
+    t0e = torch.cuda.Event(enable_timing=True)
+    t1e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t0e.record(stream)
+    for k in range(K):
+        run(args.warmup + k, k)
+    t1e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = t0e.elapsed_time(t1e)
+    ms_step = ms_total / K
+    kept.append(1.0 - float(stats["mask"].float().mean()))
+    vocab_ms = [ev["vb"][k].elapsed_time(ev["ve"][k]) for k in range(K)]
+    attn_ms = [ev["ab"][k].elapsed_time(ev["ae"][k]) for k in range(K)]
+    v_avg = float(np.mean(vocab_ms))
+    a_avg = float(np.mean(attn_ms))
+
+    alg = algorithmic(cfg)
+    achieved = alg["fl_vocab"] / (v_avg * 1e-3) / 1e12
+    traffic = read_traffic()
+    steps_s = 1000.0 / ms_step
+    out = {
+        "metric": "canvas denoise steps/s (256 tok, V=262144) + % MFMA peak, % HBM peak",
+        "value": round(steps_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; single-layer stand-in model, no trained weights)",
+        "config": {"workload": cfg.name, "canvases": cfg.B, "canvas_tokens": cfg.C, "kv_cache": cfg.L,
+                   "d_model": cfg.d, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.dh,
+                   "vocab": cfg.V, "tau": cfg.tau[0], "parallelism": "1 GPU"},
+        "canvas_tokens_per_s": round(steps_s * R, 1),
+        "step_mfma_frac": round(alg["flops"] / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "step_hbm_frac": round(alg["bytes"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "flash_vocab_ms": round(v_avg, 4),
+        "attention_ms": round(a_avg, 4),
+        "attention_mfma_frac": round(alg["fl_attn"] / (a_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "attention_hbm_frac": round(alg["by_cache"] / (a_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "kept_fraction": [round(k, 3) for k in kept],
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"kernel": "flash-vocab (logits, softmax stats, P.E)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p, cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

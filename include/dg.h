@@ -93,6 +93,11 @@ typedef struct {
   void *v_new_out;          /* [R][Hkv][dh]  canvas values */
   void *attn_out;           /* [R][Hq][dh]   O */
   void *z_out;              /* [R][d]        Z */
+  /* Optional profiling hooks: hipEvent_t handles recorded on `stream` right
+   * before and right after the main attention kernel and the main flash-vocab
+   * kernel (split combines excluded).  NULL: nothing is recorded. */
+  void *ev_attn_begin, *ev_attn_end;
+  void *ev_vocab_begin, *ev_vocab_end;
 } dg_step_io;
 
 /* Workspace bytes needed by dg_denoise_step and dg_prefill_append for dims. */

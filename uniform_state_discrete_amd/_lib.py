@@ -35,7 +35,9 @@ class Weights(ctypes.Structure):
 
 STEP_IO_FIELDS = ("H", "k_cache", "v_cache", "tokens_in", "selfcond_in", "tokens_out",
                   "selfcond_out", "max_logit", "conf", "lse", "argmax", "mask",
-                  "x_out", "q_out", "k_new_out", "v_new_out", "attn_out", "z_out")
+                  "x_out", "q_out", "k_new_out", "v_new_out", "attn_out", "z_out",
+                  "ev_attn_begin", "ev_attn_end", "ev_vocab_begin", "ev_vocab_end")
+EVENT_FIELDS = ("ev_attn_begin", "ev_attn_end", "ev_vocab_begin", "ev_vocab_end")
 
 
 class StepIO(ctypes.Structure):
@@ -110,6 +112,17 @@ def ptr(t, dtype=None):
     return t.data_ptr()
 
 
+def event_handle(ev):
+    """hipEvent_t of a torch.cuda.Event (None -> NULL).  torch creates the
+    underlying event lazily, so the event must have been recorded once."""
+    if ev is None:
+        return None
+    h = int(ev.cuda_event)
+    if h == 0:
+        raise ValueError("torch.cuda.Event has no HIP event yet: record it once first")
+    return h
+
+
 def stream_handle(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
@@ -158,7 +171,7 @@ def dg_denoise_step(dims, weights, io, tau, seed, t, block, ws, stream=None):
         if io.get(k) is not None and io[k].dtype != torch.int32:
             raise TypeError(f"{k}: expected torch.int32")
     w = Weights(*(ptr(weights[k]) for k in ("Wq", "Wk", "Wv", "Wo", "E")))
-    s = StepIO(*(ptr(io.get(k)) for k in STEP_IO_FIELDS))
+    s = StepIO(*((event_handle(io.get(k)) if k in EVENT_FIELDS else ptr(io.get(k))) for k in STEP_IO_FIELDS))
     st = lib().dg_denoise_step(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(s), float(tau),
                                int(seed), int(t), int(block), ptr(ws), ws.numel() if ws is not None else 0,
                                stream_handle(stream))

@@ -238,12 +238,13 @@ int dg_denoise_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* 
   if ((e = dg::launch_gemm_nt(dt, R, Hkv * dh, d, X, w->Wk, nullptr, Kn, s)) != hipSuccess) return hip_fail(e, "K projection");
   if ((e = dg::launch_gemm_nt(dt, R, Hkv * dh, d, X, w->Wv, nullptr, Vn, s)) != hipSuccess) return hip_fail(e, "V projection");
   dg::AttnPlan ap = dg::attn_plan(dims->B, dims->C, dims->L, dims->cap, Hq, Hkv, dh, dt, 0);
-  if ((e = dg::launch_attn(ap, Q, io->k_cache, io->v_cache, Kn, Vn, O, nullptr, scratch, s)) != hipSuccess)
+  if ((e = dg::launch_attn(ap, Q, io->k_cache, io->v_cache, Kn, Vn, O, nullptr, scratch, s,
+                           (hipEvent_t)io->ev_attn_begin, (hipEvent_t)io->ev_attn_end)) != hipSuccess)
     return hip_fail(e, "attention");
   if ((e = dg::launch_gemm_nt(dt, R, d, Hq * dh, O, w->Wo, X, Z, s)) != hipSuccess) return hip_fail(e, "output projection");
   dg::VocabPlan vp = dg::vocab_plan(R, d, dims->V, dt);
   if ((e = dg::launch_vocab(vp, Z, w->E, io->max_logit, io->argmax, io->conf, io->lse, io->selfcond_out,
-                            scratch, s)) != hipSuccess)
+                            scratch, s, (hipEvent_t)io->ev_vocab_begin, (hipEvent_t)io->ev_vocab_end)) != hipSuccess)
     return hip_fail(e, "vocab/self-conditioning");
   if ((e = dg::launch_renoise(R, dims->C, dims->V, io->argmax, io->conf, tau, seed, t, block,
                               io->tokens_out, io->mask, s)) != hipSuccess)

@@ -68,9 +68,10 @@ struct VocabPlan {
   size_t part_S_bytes, part_stat_bytes;
 };
 VocabPlan vocab_plan(int rows, int d, int V, int dtype);
+// ev_begin / ev_end (may be NULL) are recorded around the main kernel only.
 hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float* max_logit,
                         int32_t* argmax, float* conf, float* lse, void* selfcond, void* ws,
-                        hipStream_t s);
+                        hipStream_t s, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 
 struct AttnPlan {
   int B, C, L, cap, Hq, Hkv, dh, dtype, causal, nrb, nsplit, keys_per_split;
@@ -79,7 +80,7 @@ struct AttnPlan {
 AttnPlan attn_plan(int B, int C, int L, int cap, int Hq, int Hkv, int dh, int dtype, int causal);
 hipError_t launch_attn(const AttnPlan& p, const void* q, const void* kc, const void* vc,
                        const void* kn, const void* vn, void* out, float* lse, void* ws,
-                       hipStream_t s);
+                       hipStream_t s, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 
 // C[M][N] = A[M][K] . B[N][K]^T (+ Res[M][N]); dtype 0 fp32, 1 bf16.
 hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const void* B,

@@ -318,15 +318,21 @@ AttnPlan attn_plan(int B, int C, int L, int cap, int Hq, int Hkv, int dh, int dt
 
 hipError_t launch_attn(const AttnPlan& p, const void* q, const void* kc, const void* vc,
                        const void* kn, const void* vn, void* out, float* lse, void* ws,
-                       hipStream_t s) {
+                       hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end) {
   const int G = p.Hq / p.Hkv;
   const size_t nrows = (size_t)p.B * p.C * p.Hq;
   if (nrows == 0) return hipSuccess;
+  if (ev_begin) {
+    hipError_t e = hipEventRecord(ev_begin, s);
+    if (e != hipSuccess) return e;
+  }
   if (p.dtype != 1) {
     hipLaunchKernelGGL(k_attn_f32, dim3((unsigned)nrows), dim3(256), 0, s, p.B, p.C, p.L, p.cap,
                        p.Hq, p.Hkv, G, p.dh, p.causal, (const float*)q, (const float*)kc,
                        (const float*)vc, (const float*)kn, (const float*)vn, (float*)out, lse);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && ev_end) e = hipEventRecord(ev_end, s);
+    return e;
   }
   float* Opart = (float*)ws;
   float* mpart = Opart + (size_t)p.nsplit * nrows * p.dh;
@@ -343,6 +349,7 @@ hipError_t launch_attn(const AttnPlan& p, const void* q, const void* kc, const v
     DG_ATTN_LAUNCH(64);
 #undef DG_ATTN_LAUNCH
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev_end) e = hipEventRecord(ev_end, s);
   if (e != hipSuccess || p.nsplit == 1) return e;
   hipLaunchKernelGGL(k_attn_combine_bf16, dim3((unsigned)nrows), dim3(128), 0, s, (int)nrows,
                      p.nsplit, p.dh, Opart, mpart, lpart, (u16*)out, lse);

@@ -589,7 +589,7 @@ VocabPlan vocab_plan(int rows, int d, int V, int dtype) {
 
 hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float* max_logit,
                         int32_t* argmax, float* conf, float* lse, void* selfcond, void* ws,
-                        hipStream_t s) {
+                        hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (p.rows <= 0) return hipSuccess;
   if (p.variant == 0) {
     hipLaunchKernelGGL(k_vocab_f32, dim3(p.rows), dim3(256), 0, s, p.rows, p.d, p.V,
@@ -604,6 +604,10 @@ hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float*
   const u16* Eb = (const u16*)E;
   const int sl = p.d / 4;
   bool launched = true;
+  if (ev_begin) {
+    hipError_t e = hipEventRecord(ev_begin, s);
+    if (e != hipSuccess) return e;
+  }
   if (p.variant == 1) {
     switch (sl) {
       case 32: hipLaunchKernelGGL(k_vocab32<32>, grid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb, p.split_len, pS, pstat); break;
@@ -622,6 +626,7 @@ hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float*
   if (!launched) return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_vocab_combine, dim3(p.rows), dim3(256), 0, s, p.rows, p.d, p.nsplit, pS,
                      pstat, max_logit, argmax, conf, lse, selfcond, 1);
   return hipGetLastError();
