@@ -62,13 +62,12 @@ def read_traffic():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(p, cfg, rows=8):
-    """The oracle, as it stands, on a bounded sample of the same step: the
-    assemble and K/V projections for every canvas row (the keys need them) and
-    Q, attention, Z, vocabulary head, self-conditioning and renoise for `rows`
-    rows; the per-row part is scaled to the full canvas."""
+def cpu_baseline(p, cfg, min_seconds=10.0):
+    """The oracle, as it stands, timed on the host: whole denoise steps of the
+    same workload (chained like the GPU's), repeated until min_seconds have
+    passed (at least one step)."""
     import numpy as np
-    from oracle import numerics, philox, step
+    from oracle import step
     from synth import from_storage
     try:
         from threadpoolctl import threadpool_info
@@ -78,32 +77,19 @@ def cpu_baseline(p, cfg, rows=8):
     f = lambda a: from_storage(a, cfg.dtype).astype(np.float64)
     E, H, Kc, Vc = f(p.E), f(p.H[0]), f(p.Kc), f(p.Vc)
     W = {k: f(v) for k, v in p.W.items()}
-    R = cfg.B * cfg.C
     x = step.init_canvas(cfg.seed, 0, cfg.B, cfg.C, cfg.V)
+    S = None
+    n = 0
     t0 = time.perf_counter()
-    X = step.assemble(H, E, x, None, cfg.dtype).reshape(R, cfg.d)
-    Kn = step.linear(X, W["Wk"], cfg.dtype).reshape(cfg.B, cfg.C, cfg.Hkv, cfg.dh)
-    Vn = step.linear(X, W["Wv"], cfg.dtype).reshape(cfg.B, cfg.C, cfg.Hkv, cfg.dh)
-    t1 = time.perf_counter()
-    sel = np.arange(rows) * (R // rows)
-    Q = step.linear(X[sel], W["Wq"], cfg.dtype).reshape(rows, cfg.Hq, cfg.dh)
-    O = np.empty((rows, cfg.Hq * cfg.dh))
-    for n, r in enumerate(sel):
-        b, i = divmod(int(r), cfg.C)
-        for h in range(cfg.Hq):
-            o, _ = step.attention_row(Q[n, h], b, h // cfg.G, i, Kc, Vc, Kn, Vn, cfg.L, False)
-            O[n, h * cfg.dh:(h + 1) * cfg.dh] = o
-    Z = numerics.round_store(X[sel] + numerics.round_store(O, cfg.dtype) @ W["Wo"].T, cfg.dtype)
-    m, a, lse, c, S, _ = step.vocab_rows(Z, E)
-    for n, r in enumerate(sel):
-        if c[n] < np.float32(cfg.tau[0]):
-            philox.uniform_token(cfg.seed, 1, int(r) // cfg.C, 0, int(r) % cfg.C, cfg.V)
-    t2 = time.perf_counter()
-    per_step = (t1 - t0) + (t2 - t1) * (R / rows)
-    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"numpy fp64 oracle, one step of {cfg.name}: assemble + K/V projections for all "
-                      f"{R} rows ({t1 - t0:.2f} s) + Q/attention/Z/vocab/self-conditioning/renoise for "
-                      f"{rows} rows ({t2 - t1:.2f} s) scaled x{R // rows}; est. {per_step:.1f} s/step"}
+    while True:
+        r = step.denoise_step(H, E, W, Kc, Vc, cfg.L, x, S, cfg.tau[0], cfg.seed, n + 1, 0, cfg.dtype)
+        x, S = r["x_new"], r["S"]
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": n / el, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} whole numpy fp64 oracle step(s) of {cfg.name}, chained, {el:.1f} s"}
 
 
 def copy_calibration(mib):
@@ -233,7 +219,9 @@ def main():
         "wall_s_timed": round(wall, 3),
         "roofline": {"kernel": "flash-vocab (logits, softmax stats, P.E)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                     "algorithmic_bytes": alg["by_E"] + cfg.B * cfg.C * cfg.d * 2.0},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, cfg)

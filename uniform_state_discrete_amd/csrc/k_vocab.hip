@@ -8,10 +8,20 @@
 
 namespace dg {
 
-// Rescale threshold (natural-log units): the running reference max of a row
-// is only moved when a new logit exceeds it by more than this, so that
-// P = exp(l - m_ref) stays <= e^8 and the accumulator is rarely rescaled.
-constexpr float kLazyTh = 8.0f;
+// Rescale threshold (natural-log units): a row's reference max only moves
+// when a new logit exceeds it by more than this.  P = exp(l - m_ref) then
+// stays <= e^40, and a sum of up to 2^24 such terms times |E| stays far below
+// FLT_MAX; terms more than ~87 below the reference underflow, and they are
+// then more than 87 below the row's maximum too (negligible in fp32).
+constexpr float kLazyTh = 40.0f;
+
+// LDS row of E-tile row m.  Rows are padded by 16 bytes, so the 64 banks see
+// (row + 16-byte unit) mod 16; permuting the rows keeps both access patterns
+// conflict-free: 16 lanes writing one unit of 16 consecutive tile rows, and
+// the transposing reads of 4 (32-row tiles) or 8 (16-row tiles) consecutive
+// tile rows x 32 bytes per 32 lanes.  Column offsets stay compile-time.
+__device__ __forceinline__ int prow32(int m) { return 4 * (m & 3) + ((m >> 2) & 3) + 16 * (m >> 4); }
+__device__ __forceinline__ int prow16(int m) { return 2 * (m & 7) + (m >> 3); }
 
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma16x32(u32x4 a, u32x4 b, f32x4 c) {
@@ -64,10 +74,10 @@ template <int SLICE>
 __global__ void __launch_bounds__(256, 1)
     k_vocab32(const u16* __restrict__ Z, const u16* __restrict__ E, int R, int d, int V, int nrb,
               int split_len, float* __restrict__ pS, f32x4* __restrict__ pstat) {
-  constexpr int NCH = SLICE / 32, KSN = SLICE / 16, EP = SLICE + 32;
+  constexpr int NCH = SLICE / 32, KSN = SLICE / 16, EP = SLICE + 8;
   constexpr int PF = NCH < 4 ? NCH : (SLICE >= 512 ? 2 : 4);  // chunks of E in flight
   __shared__ __attribute__((aligned(16))) u16 Et[4][32][EP];
-  __shared__ __attribute__((aligned(16))) float xch[4][64][16];
+  __shared__ __attribute__((aligned(16))) f32x4 xch[4][4][64];  // [wave][16-byte chunk][lane]
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, l32 = l & 31;
   int rb, split;
@@ -91,9 +101,14 @@ __global__ void __launch_bounds__(256, 1)
   DG_LDS u16* et = (DG_LDS u16*)&Et[w][0][0];
   const int nt = ve > vs ? (ve - vs + 31) / 32 : 0;
   for (int e = l * 8; e < 32 * EP; e += 64 * 8) *(DG_LDS u32x4*)(et + e) = z4;
-  // transposing-read coordinates of this lane inside a 32-column chunk
+  // transposing-read addresses of this lane: tile rows tr_r + {0, 8, 16, 24},
+  // column 16*((l>>4)&1) + 4*(l&3) inside each 32-column chunk
   const int tr_r = 4 * h + ((l & 15) >> 2);
   const int tr_c = 16 * ((l >> 4) & 1) + (l & 3) * 4;
+  const DG_LDS u16* trb[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) trb[s] = et + prow32(tr_r + 8 * s) * EP + tr_c;
+  DG_LDS u16* wrb = et + prow32(l32) * EP + h * 8;
 
   // E fragments of chunk c (columns [32c, 32c+32) of the slice) of a tile live
   // in ring slot c % PF; they are issued PF chunks ahead of their use.
@@ -120,10 +135,10 @@ __global__ void __launch_bounds__(256, 1)
   auto gather_logits = [&](int v0, float* L) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      f32x4 a = *(const f32x4*)&xch[0][l][4 * q];
-      a += *(const f32x4*)&xch[1][l][4 * q];
-      a += *(const f32x4*)&xch[2][l][4 * q];
-      a += *(const f32x4*)&xch[3][l][4 * q];
+      f32x4 a = xch[0][q][l];
+      a += xch[1][q][l];
+      a += xch[2][q][l];
+      a += xch[3][q][l];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int v = v0 + 8 * q + 4 * h + i;  // element 4q+i is id v0 + 8q + 4h + i
@@ -135,7 +150,8 @@ __global__ void __launch_bounds__(256, 1)
     float pv[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      pv[e] = L[e] == -INFINITY ? 0.f : round_bf16(exp2f((L[e] - m_seg) * kLog2e));
+      // the normaliser sums the fp32 probabilities; bf16 copies feed P.E
+      pv[e] = L[e] == -INFINITY ? 0.f : exp2f((L[e] - m_seg) * kLog2e);
       lsum += pv[e];
     }
     pf0 = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
@@ -163,13 +179,12 @@ __global__ void __launch_bounds__(256, 1)
         lg = mfma32(e1, zf[2 * c + 1], lg);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const DG_LDS u16* q = et + (16 * p + tr_r) * EP + c * 32 + tr_c;
-          const u32x2 a0 = lds_read_tr16(q);
-          const u32x2 a1 = lds_read_tr16(q + 8 * EP);
+          const u32x2 a0 = lds_read_tr16(trb[2 * p] + c * 32);
+          const u32x2 a1 = lds_read_tr16(trb[2 * p + 1] + c * 32);
           acc[c] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, p ? pf1 : pf0, acc[c]);
         }
-        *(DG_LDS u32x4*)(et + l32 * EP + c * 32 + h * 8) = e0;
-        *(DG_LDS u32x4*)(et + l32 * EP + c * 32 + 16 + h * 8) = e1;
+        *(DG_LDS u32x4*)(wrb + c * 32) = e0;
+        *(DG_LDS u32x4*)(wrb + c * 32 + 16) = e1;
         if (c + PF < NCH)
           issue(slot, t, c + PF);
         else
@@ -181,7 +196,7 @@ __global__ void __launch_bounds__(256, 1)
       // sum the four d-slice partials
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *(f32x4*)&xch[w][l][4 * q] = f32x4{lg[4 * q], lg[4 * q + 1], lg[4 * q + 2], lg[4 * q + 3]};
+        xch[w][q][l] = f32x4{lg[4 * q], lg[4 * q + 1], lg[4 * q + 2], lg[4 * q + 3]};
       __syncthreads();
       const int v0 = vs + t * 32;
       float L[16];
@@ -269,10 +284,10 @@ template <int SLICE>
 __global__ void __launch_bounds__(256, 1)
     k_vocab16(const u16* __restrict__ Z, const u16* __restrict__ E, int R, int d, int V, int nrb,
               int split_len, float* __restrict__ pS, f32x4* __restrict__ pstat) {
-  constexpr int NCH = SLICE / 32, EP = SLICE + 32;
+  constexpr int NCH = SLICE / 32, EP = SLICE + 8;
   constexpr int PF = NCH < 8 ? NCH : 8;
   __shared__ __attribute__((aligned(16))) u16 Et[4][16][EP];
-  __shared__ __attribute__((aligned(16))) float xch[4][64][4];
+  __shared__ __attribute__((aligned(16))) f32x4 xch[4][64];
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g4 = l >> 4, l16 = l & 15;
   int rb, split;
@@ -296,7 +311,8 @@ __global__ void __launch_bounds__(256, 1)
   const int nt = ve > vs ? (ve - vs + 15) / 16 : 0;
   for (int e = l * 8; e < 16 * EP; e += 64 * 8) *(DG_LDS u32x4*)(et + e) = z4;
   const int tr_r = 4 * g4 + (l16 >> 2);
-  const int tr_c = (l & 3) * 4;
+  const DG_LDS u16* trb = et + prow16(tr_r) * EP + (l & 3) * 4;
+  DG_LDS u16* wrb = et + prow16(l16) * EP + g4 * 8;
 
   u32x4 ring0[PF];
   auto issue = [&](int slot, int tile, int c) {
@@ -313,10 +329,10 @@ __global__ void __launch_bounds__(256, 1)
   u32x2 pf = {0u, 0u};
 
   auto gather_logits = [&](int v0, float* L) {
-    f32x4 a = *(const f32x4*)&xch[0][l][0];
-    a += *(const f32x4*)&xch[1][l][0];
-    a += *(const f32x4*)&xch[2][l][0];
-    a += *(const f32x4*)&xch[3][l][0];
+    f32x4 a = xch[0][l];
+    a += xch[1][l];
+    a += xch[2][l];
+    a += xch[3][l];
 #pragma unroll
     for (int i = 0; i < 4; ++i) L[i] = (v0 + 4 * g4 + i) < ve ? a[i] : -INFINITY;  // id v0 + 4*g4 + i
   };
@@ -324,7 +340,7 @@ __global__ void __launch_bounds__(256, 1)
     float pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pv[i] = L[i] == -INFINITY ? 0.f : round_bf16(exp2f((L[i] - m_seg) * kLog2e));
+      pv[i] = L[i] == -INFINITY ? 0.f : exp2f((L[i] - m_seg) * kLog2e);
       lsum += pv[i];
     }
     pf = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
@@ -346,10 +362,10 @@ __global__ void __launch_bounds__(256, 1)
         lg = mfma16x32(e0, zf[c], lg);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const u32x2 a = lds_read_tr16(et + tr_r * EP + c * 32 + 16 * p + tr_c);
+          const u32x2 a = lds_read_tr16(trb + c * 32 + 16 * p);
           acc[2 * c + p] = mfma16x16(a, pf, acc[2 * c + p]);
         }
-        *(DG_LDS u32x4*)(et + l16 * EP + c * 32 + g4 * 8) = e0;
+        *(DG_LDS u32x4*)(wrb + c * 32) = e0;
         if (c + PF < NCH)
           issue(slot, t, c + PF);
         else
@@ -358,7 +374,7 @@ __global__ void __launch_bounds__(256, 1)
       }
       if (!have) break;
 
-      *(f32x4*)&xch[w][l][0] = lg;
+      xch[w][l] = lg;
       __syncthreads();
       const int v0 = vs + t * 16;
       float L[4];
