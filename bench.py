@@ -132,6 +132,7 @@ def main():
     p = gen_problem(cfg)
     W = {k: dg.to_device(v) for k, v in p.W.items()}
     W["E"] = dg.to_device(p.E)
+    W["E_tiled"] = dg.tiled_embedding(W["E"])   # once per model, outside any timed region
     Kc, Vc, H = dg.to_device(p.Kc), dg.to_device(p.Vc), dg.to_device(p.H[0])
     fdt = W["E"].dtype
     code = dg.DG_BF16 if cfg.dtype == "bf16" else dg.DG_F32

@@ -67,9 +67,13 @@ typedef struct {
 
 /* Model tensors.  Projection weights are stored output-major, like a linear
  * layer's weight: Wq[Hq*dh][d], Wk[Hkv*dh][d], Wv[Hkv*dh][d], Wo[d][Hq*dh].
- * E[V][d] is the token-embedding table, also the tied vocabulary head. */
+ * E[V][d] is the token-embedding table, also the tied vocabulary head.
+ * E_tiled is the same table in the tiled layout of dg_pack_embedding, read by
+ * the bf16 vocabulary head (the row-major E serves the token gathers);
+ * required for DG_BF16, ignored for DG_F32. */
 typedef struct {
   const void *Wq, *Wk, *Wv, *Wo, *E;
+  const void *E_tiled;
 } dg_weights;
 
 /* Per-step tensors (R = B*C rows, row r = canvas r / C, position r % C). */
@@ -128,12 +132,28 @@ int dg_attn_bidir(const dg_dims *dims, const void *q, const void *k_cache, const
                   const void *k_new, const void *v_new, void *out, float *lse_out, int causal,
                   void *ws, size_t ws_bytes, void *stream);
 
+/* Tiled layout of a bf16 embedding table for the vocabulary head.  E[V][d]
+ * (row-major) is cut into blocks of 16 ids x 32 columns; block (vb, c) is
+ * 1 KiB at byte offset (vb * (d / 32) + c) * 1024, and inside it entry
+ * (id 16 vb + r, column 32 c + 8 g + e) sits at element 8 (16 g + r) + e
+ * (g < 4, r < 16, e < 8).  Ids in [V, 16 ceil(V/16)) read as zero.  The
+ * vocabulary kernels load one block per instruction, 1 KiB contiguous, in
+ * the lane order of their matrix-core operands.  Needs d % 32 == 0.
+ * dg_tiled_embedding_bytes returns 16 ceil(V/16) d 2 (0 for invalid sizes or
+ * DG_F32, which has no tiled layout); dg_pack_embedding writes E_tiled
+ * (that many bytes, 16-byte aligned, not overlapping E) from E. */
+size_t dg_tiled_embedding_bytes(int32_t V, int32_t d, int32_t dtype);
+int dg_pack_embedding(int32_t V, int32_t d, int32_t dtype, const void *E, void *E_tiled,
+                      void *stream);
+
 /* Vocabulary head, confidence and self-conditioning ("Autocondizionamento";
  * confidence as in "Diffusione dello stato uniforme"): for each of `rows`
- * rows of z[rows][d] and E[V][d]: logits l = z E^T,
+ * rows of z[rows][d] and the table E[V][d]: logits l = z E^T,
  * max_logit = max l, argmax = lowest id attaining it, lse = log sum exp l,
  * conf = exp(max_logit - lse), selfcond[rows][d] = softmax(l) E.
- * The rows x V probability matrix is never stored.  lse may be NULL. */
+ * The rows x V probability matrix is never stored.  lse may be NULL.
+ * E is the row-major table for DG_F32 and the tiled table of
+ * dg_pack_embedding for DG_BF16. */
 size_t dg_vocab_workspace_bytes(int32_t rows, int32_t d, int32_t V, int32_t dtype);
 int dg_vocab_selfcond(int32_t rows, int32_t d, int32_t V, int32_t dtype, const void *z,
                       const void *E, float *max_logit, int32_t *argmax, float *conf, float *lse,

@@ -71,7 +71,7 @@ def test_workspace_sizes(L):
 
 def _step(L, d, ws_bytes=1 << 40, null=(), weights_null=(), ws=FAKE):
     lib = L.lib()
-    w = L.Weights(*[None if k in weights_null else FAKE for k in ("Wq", "Wk", "Wv", "Wo", "E")])
+    w = L.Weights(*[None if k in weights_null else FAKE for k in L.WEIGHT_FIELDS])
     io = L.StepIO(*[None if (k in null or k in ("selfcond_in", "lse", "mask", "x_out", "q_out",
                                                  "k_new_out", "v_new_out", "attn_out", "z_out"))
                     else FAKE for k in L.STEP_IO_FIELDS])
@@ -83,6 +83,7 @@ def test_step_argument_checks(L):
     lib = L.lib()
     assert _step(L, dims(), null=("H",)) == L.DG_EINVAL
     assert _step(L, dims(), weights_null=("E",)) == L.DG_EINVAL
+    assert _step(L, dims(), weights_null=("E_tiled",)) == L.DG_EINVAL   # bf16 needs the tiled table
     assert _step(L, dims(n_kv_heads=3)) == L.DG_EINVAL
     assert _step(L, dims(B=0)) == L.DG_EINVAL
     assert _step(L, dims(L=2000, cap=1024)) == L.DG_EINVAL
@@ -93,7 +94,7 @@ def test_step_argument_checks(L):
     assert _step(L, dims(), ws=None) == L.DG_EWORKSPACE
     assert b"workspace" in lib.dg_last_error()
     # misaligned bf16 tensor
-    w = L.Weights(FAKE, FAKE + 2, FAKE, FAKE, FAKE)
+    w = L.Weights(FAKE, FAKE + 2, FAKE, FAKE, FAKE, FAKE)
     io = L.StepIO(*[FAKE if k in ("H", "k_cache", "v_cache", "tokens_in", "tokens_out", "selfcond_out",
                                   "max_logit", "conf", "argmax") else None for k in L.STEP_IO_FIELDS])
     st = lib.dg_denoise_step(ctypes.byref(dims()), ctypes.byref(w), ctypes.byref(io), 0.9, 1, 1, 0,
@@ -119,7 +120,23 @@ def test_component_argument_checks(L):
     assert lib.dg_renoise(16, 16, 100, None, FAKE, 0.5, 1, 1, 0, FAKE, None, None) == L.DG_EINVAL
     assert lib.dg_init_canvas(16, 16, 0, 1, 0, FAKE, None) == L.DG_EINVAL
     # append beyond the cache capacity
-    w = L.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
+    w = L.Weights(FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert lib.dg_prefill_append(ctypes.byref(dims(L=1000, cap=1024)), ctypes.byref(w), FAKE, FAKE, FAKE,
                                  FAKE, None, FAKE, 1 << 40, None) == L.DG_EINVAL
     assert b"cap" in lib.dg_last_error()
+
+
+def test_tiled_embedding_sizes_and_checks(L):
+    lib = L.lib()
+    vp = ctypes.c_void_p
+    # 16-id x 32-column blocks: V rounds up to a multiple of 16
+    assert L.dg_tiled_embedding_bytes(262144, 2048, L.DG_BF16) == 262144 * 2048 * 2
+    assert L.dg_tiled_embedding_bytes(3000, 256, L.DG_BF16) == 3008 * 256 * 2
+    assert L.dg_tiled_embedding_bytes(100, 2048, L.DG_F32) == 0      # no tiled fp32 layout
+    assert L.dg_tiled_embedding_bytes(100, 100, L.DG_BF16) == 0      # d % 32 != 0
+    assert lib.dg_pack_embedding(100, 64, L.DG_F32, vp(FAKE), vp(FAKE * 4), None) == L.DG_EUNSUPPORTED
+    assert lib.dg_pack_embedding(100, 100, L.DG_BF16, vp(FAKE), vp(FAKE * 4), None) == L.DG_EINVAL
+    assert lib.dg_pack_embedding(100, 64, L.DG_BF16, None, vp(FAKE * 4), None) == L.DG_EINVAL
+    assert lib.dg_pack_embedding(100, 64, L.DG_BF16, vp(FAKE), vp(FAKE + 8), None) == L.DG_EINVAL  # aligned
+    assert lib.dg_pack_embedding(100, 64, L.DG_BF16, vp(FAKE), vp(FAKE + 4096), None) == L.DG_EINVAL  # overlap
+    assert b"overlap" in lib.dg_last_error()

@@ -72,9 +72,29 @@ def _run_vocab(R, d, V, E, Z, dtype):
     a = torch.empty(R, dtype=torch.int32, device="cuda")
     S = torch.empty((R, d), dtype=Zd.dtype, device="cuda")
     ws = dg.workspace(dg.dg_vocab_workspace_bytes(R, d, V, Zd.dtype))
-    dg.dg_vocab_selfcond(R, d, V, Zd, Ed, m, a, c, lse, S, ws)
+    Et = dg.tiled_embedding(Ed)
+    dg.dg_vocab_selfcond(R, d, V, Zd, Ed if Et is None else Et, m, a, c, lse, S, ws)
     torch.cuda.synchronize()
     return f64(m), a.cpu().numpy(), f64(c), f64(lse), f64(S)
+
+
+@pytest.mark.parametrize("V,d", [(37, 64), (3000, 256), (16, 4096)])
+def test_tiled_embedding_layout(V, d):
+    """The tiled table holds, at element 8(16g + r) + e of 1 KiB block
+    (vb, c), entry (16 vb + r, 32 c + 8 g + e) of E, zero past V."""
+    import uniform_state_discrete_amd as dg
+    say(f"tiled embedding V={V} d={d}")
+    r = np.random.default_rng(V + d)
+    E = stored(r.standard_normal((V, d)).astype(np.float32), "bf16")
+    Et = dg.tiled_embedding(dev(E))
+    torch.cuda.synchronize()
+    got = Et.view(torch.int16).cpu().numpy().view(np.uint16)
+    Vp = -(-V // 16) * 16
+    ref = np.zeros((Vp, d), dtype=np.uint16)
+    ref[:V] = E
+    # blocks [vb][c][g][r][e] <- ref[16 vb + r][32 c + 8 g + e]
+    ref = ref.reshape(Vp // 16, 16, d // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    assert np.array_equal(got, ref)
 
 
 @pytest.mark.parametrize("R,d,V,dtype", [

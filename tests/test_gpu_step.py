@@ -37,6 +37,7 @@ class Dev:
         self.cfg = c
         self.W = {k: dev(v) for k, v in p.W.items()}
         self.W["E"] = dev(p.E)
+        self.W["E_tiled"] = dg.tiled_embedding(self.W["E"])
         self.Kc = dev(p.Kc)
         self.Vc = dev(p.Vc)
         self.H = [dev(h) for h in p.H]

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     lib, make_dims, workspace, ptr, dtype_code, stream_handle,
     dg_workspace_bytes, dg_attn_workspace_bytes, dg_vocab_workspace_bytes,
     dg_denoise_step, dg_attn_bidir, dg_vocab_selfcond, dg_renoise, dg_init_canvas,
-    dg_prefill_append,
+    dg_prefill_append, dg_tiled_embedding_bytes, dg_pack_embedding, tiled_embedding,
+    WEIGHT_FIELDS,
 )
 from .device import to_device, torch_dtype  # noqa: F401

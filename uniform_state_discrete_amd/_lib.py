@@ -29,8 +29,11 @@ class Dims(ctypes.Structure):
                 ("B", "C", "L", "cap", "d", "n_q_heads", "n_kv_heads", "head_dim", "V", "dtype")]
 
 
+WEIGHT_FIELDS = ("Wq", "Wk", "Wv", "Wo", "E", "E_tiled")
+
+
 class Weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("Wq", "Wk", "Wv", "Wo", "E")]
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
 
 
 STEP_IO_FIELDS = ("H", "k_cache", "v_cache", "tokens_in", "selfcond_in", "tokens_out",
@@ -63,6 +66,8 @@ def lib():
             "dg_workspace_bytes": (sz, [pd]),
             "dg_attn_workspace_bytes": (sz, [pd]),
             "dg_vocab_workspace_bytes": (sz, [i32, i32, i32, i32]),
+            "dg_tiled_embedding_bytes": (sz, [i32, i32, i32]),
+            "dg_pack_embedding": (ctypes.c_int, [i32, i32, i32, vp, vp, vp]),
             "dg_denoise_step": (ctypes.c_int, [pd, ctypes.POINTER(Weights), ctypes.POINTER(StepIO),
                                                f32, u64, u32, u32, vp, sz, vp]),
             "dg_attn_bidir": (ctypes.c_int, [pd, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]),
@@ -151,6 +156,29 @@ def dg_vocab_workspace_bytes(rows, d, V, dtype):
     return lib().dg_vocab_workspace_bytes(rows, d, V, dtype if isinstance(dtype, int) else dtype_code(dtype))
 
 
+def dg_tiled_embedding_bytes(V, d, dtype):
+    return lib().dg_tiled_embedding_bytes(int(V), int(d), dtype if isinstance(dtype, int) else dtype_code(dtype))
+
+
+def dg_pack_embedding(V, d, E, E_tiled, stream=None):
+    st = lib().dg_pack_embedding(int(V), int(d), dtype_code(E.dtype), ptr(E), ptr(E_tiled), stream_handle(stream))
+    _check(st, "dg_pack_embedding")
+
+
+def tiled_embedding(E, stream=None):
+    """A new device tensor holding bf16 table E[V][d] in the tiled layout the
+    vocabulary head reads (dg_pack_embedding); None for a float32 table."""
+    if E.dtype != torch.bfloat16:
+        return None
+    V, d = E.shape
+    n = dg_tiled_embedding_bytes(V, d, E.dtype)
+    if n == 0:
+        raise DgError(DG_EUNSUPPORTED, "tiled_embedding", f"no tiled layout for V={V} d={d}")
+    out = torch.empty(n // 2, dtype=torch.bfloat16, device=E.device)
+    dg_pack_embedding(V, d, E, out, stream)
+    return out
+
+
 _FLOAT_IO = ("H", "k_cache", "v_cache", "selfcond_in", "selfcond_out", "x_out", "q_out",
              "k_new_out", "v_new_out", "attn_out", "z_out")
 
@@ -163,14 +191,15 @@ def _check_float_dtype(dims, tensors):
 
 
 def dg_denoise_step(dims, weights, io, tau, seed, t, block, ws, stream=None):
-    """weights: dict Wq, Wk, Wv, Wo, E; io: dict with the dg_step_io fields
-    (missing keys -> NULL).  ws: uint8 workspace tensor."""
-    _check_float_dtype(dims, [(k, weights.get(k)) for k in ("Wq", "Wk", "Wv", "Wo", "E")] +
+    """weights: dict Wq, Wk, Wv, Wo, E (and E_tiled for bf16, see
+    tiled_embedding); io: dict with the dg_step_io fields (missing keys ->
+    NULL).  ws: uint8 workspace tensor."""
+    _check_float_dtype(dims, [(k, weights.get(k)) for k in WEIGHT_FIELDS] +
                        [(k, io.get(k)) for k in _FLOAT_IO])
     for k in ("tokens_in", "tokens_out", "argmax"):
         if io.get(k) is not None and io[k].dtype != torch.int32:
             raise TypeError(f"{k}: expected torch.int32")
-    w = Weights(*(ptr(weights[k]) for k in ("Wq", "Wk", "Wv", "Wo", "E")))
+    w = Weights(*(ptr(weights.get(k)) for k in WEIGHT_FIELDS))
     s = StepIO(*((event_handle(io.get(k)) if k in EVENT_FIELDS else ptr(io.get(k))) for k in STEP_IO_FIELDS))
     st = lib().dg_denoise_step(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(s), float(tau),
                                int(seed), int(t), int(block), ptr(ws), ws.numel() if ws is not None else 0,
@@ -186,6 +215,8 @@ def dg_attn_bidir(dims, q, k_cache, v_cache, k_new, v_new, out, lse_out, causal,
 
 
 def dg_vocab_selfcond(rows, d, V, z, E, max_logit, argmax, conf, lse, selfcond, ws, stream=None):
+    """E: the row-major float32 table, or for bf16 the tiled table of
+    tiled_embedding."""
     st = lib().dg_vocab_selfcond(int(rows), int(d), int(V), dtype_code(z.dtype), ptr(z), ptr(E),
                                  ptr(max_logit, torch.float32), ptr(argmax, torch.int32),
                                  ptr(conf, torch.float32), ptr(lse, torch.float32), ptr(selfcond),
@@ -207,7 +238,7 @@ def dg_init_canvas(rows, canvas, V, seed, block, tokens_out, stream=None):
 
 
 def dg_prefill_append(dims, weights, H, tokens_final, k_cache, v_cache, attn_out, ws, stream=None):
-    w = Weights(*(ptr(weights.get(k)) for k in ("Wq", "Wk", "Wv", "Wo", "E")))
+    w = Weights(*(ptr(weights.get(k)) for k in WEIGHT_FIELDS))
     st = lib().dg_prefill_append(ctypes.byref(dims), ctypes.byref(w), ptr(H), ptr(tokens_final, torch.int32),
                                  ptr(k_cache), ptr(v_cache), ptr(attn_out), ptr(ws),
                                  ws.numel() if ws is not None else 0, stream_handle(stream))

@@ -58,6 +58,8 @@ int check_vocab_shape(int rows, int d, int V, int dtype) {
   if (dtype == DG_BF16) {
     if (!(d == 128 || d == 256 || d == 512 || d == 1024 || d == 2048 || d == 4096))
       return fail(DG_EUNSUPPORTED, "bf16 vocab head needs d in {128,256,512,1024,2048,4096} (got %d)", d);
+    if (((size_t)V + 15) / 16 * 16 * (size_t)d * 2 > 0xFFFF0000u)
+      return fail(DG_EUNSUPPORTED, "bf16 vocab head needs a table under 4 GiB (V=%d d=%d)", V, d);
     dg::VocabPlan p = dg::vocab_plan(rows, d, V, dtype);
     if (p.nsplit > kMaxSplits) return fail(DG_EUNSUPPORTED, "too many vocab splits");
   } else {
@@ -164,6 +166,23 @@ int dg_init_canvas(int32_t rows, int32_t canvas, int32_t V, uint64_t seed, uint3
   return e == hipSuccess ? DG_OK : hip_fail(e, "dg_init_canvas");
 }
 
+size_t dg_tiled_embedding_bytes(int32_t V, int32_t d, int32_t dtype) {
+  if (dtype != DG_BF16 || V <= 0 || d <= 0 || d % 32) return 0;
+  return ((size_t)V + 15) / 16 * 16 * (size_t)d * 2;
+}
+
+int dg_pack_embedding(int32_t V, int32_t d, int32_t dtype, const void* E, void* E_tiled, void* stream) {
+  if (dtype != DG_BF16) return fail(DG_EUNSUPPORTED, "only bf16 tables have a tiled layout");
+  if (V <= 0 || d <= 0 || d % 32) return fail(DG_EINVAL, "need V > 0 and d %% 32 == 0 (V=%d d=%d)", V, d);
+  if (!E || !E_tiled) return fail(DG_EINVAL, "E and E_tiled must be non-NULL");
+  if (!aligned16(E) || !aligned16(E_tiled)) return fail(DG_EINVAL, "E and E_tiled must be 16-byte aligned");
+  const size_t n = dg_tiled_embedding_bytes(V, d, dtype);
+  const char *a = (const char*)E, *b = (const char*)E_tiled;
+  if (a < b + n && b < a + (size_t)V * d * 2) return fail(DG_EINVAL, "E_tiled must not overlap E");
+  hipError_t e = dg::launch_pack_embedding(V, d, E, E_tiled, (hipStream_t)stream);
+  return e == hipSuccess ? DG_OK : hip_fail(e, "dg_pack_embedding");
+}
+
 int dg_vocab_selfcond(int32_t rows, int32_t d, int32_t V, int32_t dtype, const void* z,
                       const void* E, float* max_logit, int32_t* argmax, float* conf, float* lse,
                       void* selfcond, void* ws, size_t ws_bytes, void* stream) {
@@ -205,7 +224,8 @@ int dg_denoise_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* 
   int st = check_dims(dims, true);
   if (st != DG_OK) return st;
   if (!w || !io) return fail(DG_EINVAL, "weights and io must be non-NULL");
-  if (!w->Wq || !w->Wk || !w->Wv || !w->Wo || !w->E) return fail(DG_EINVAL, "every weight pointer must be non-NULL");
+  if (!w->Wq || !w->Wk || !w->Wv || !w->Wo || !w->E || (dims->dtype == DG_BF16 && !w->E_tiled))
+    return fail(DG_EINVAL, "every weight pointer (and E_tiled for bf16) must be non-NULL");
   if (!io->H || !io->tokens_in || !io->tokens_out || !io->selfcond_out || !io->max_logit ||
       !io->conf || !io->argmax || (dims->L > 0 && (!io->k_cache || !io->v_cache)))
     return fail(DG_EINVAL, "H, tokens_in/out, selfcond_out, max_logit, conf, argmax (and the caches when L > 0) must be non-NULL");
@@ -215,8 +235,8 @@ int dg_denoise_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* 
     return fail(DG_EUNSUPPORTED, "bf16 step needs d %% 128 == 0 and n_q_heads*head_dim %% 64 == 0");
   const void* ptrs[] = {w->Wq, w->Wk, w->Wv, w->Wo, w->E, io->H, io->k_cache, io->v_cache,
                         io->selfcond_in, io->selfcond_out, io->x_out, io->q_out, io->k_new_out,
-                        io->v_new_out, io->attn_out, io->z_out};
-  if ((st = check_bf16_align(dims, ptrs, 16)) != DG_OK) return st;
+                        io->v_new_out, io->attn_out, io->z_out, w->E_tiled};
+  if ((st = check_bf16_align(dims, ptrs, 17)) != DG_OK) return st;
   const StepLayout L = step_layout(dims);
   if (!ws || ws_bytes < L.total)
     return fail(DG_EWORKSPACE, "step workspace needs %zu bytes (got %zu)", L.total, ws ? ws_bytes : 0);
@@ -243,7 +263,7 @@ int dg_denoise_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* 
     return hip_fail(e, "attention");
   if ((e = dg::launch_gemm_nt(dt, R, d, Hq * dh, O, w->Wo, X, Z, s)) != hipSuccess) return hip_fail(e, "output projection");
   dg::VocabPlan vp = dg::vocab_plan(R, d, dims->V, dt);
-  if ((e = dg::launch_vocab(vp, Z, w->E, io->max_logit, io->argmax, io->conf, io->lse, io->selfcond_out,
+  if ((e = dg::launch_vocab(vp, Z, dt == DG_BF16 ? w->E_tiled : w->E, io->max_logit, io->argmax, io->conf, io->lse, io->selfcond_out,
                             scratch, s, (hipEvent_t)io->ev_vocab_begin, (hipEvent_t)io->ev_vocab_end)) != hipSuccess)
     return hip_fail(e, "vocab/self-conditioning");
   if ((e = dg::launch_renoise(R, dims->C, dims->V, io->argmax, io->conf, tau, seed, t, block,

@@ -82,6 +82,10 @@ hipError_t launch_attn(const AttnPlan& p, const void* q, const void* kc, const v
                        const void* kn, const void* vn, void* out, float* lse, void* ws,
                        hipStream_t s, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 
+// Tiled bf16 embedding table (16-id x 32-column blocks of 1 KiB in operand
+// lane order); see dg_pack_embedding.
+hipError_t launch_pack_embedding(int V, int d, const void* E, void* E_tiled, hipStream_t s);
+
 // C[M][N] = A[M][K] . B[N][K]^T (+ Res[M][N]); dtype 0 fp32, 1 bf16.
 hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const void* B,
                           const void* Res, void* C, hipStream_t s);

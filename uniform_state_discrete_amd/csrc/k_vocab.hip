@@ -16,12 +16,13 @@ namespace dg {
 constexpr float kLazyTh = 40.0f;
 
 // LDS row of E-tile row m.  Rows are padded by 16 bytes, so the 64 banks see
-// (row + 16-byte unit) mod 16; permuting the rows keeps both access patterns
-// conflict-free: 16 lanes writing one unit of 16 consecutive tile rows, and
-// the transposing reads of 4 (32-row tiles) or 8 (16-row tiles) consecutive
-// tile rows x 32 bytes per 32 lanes.  Column offsets stay compile-time.
-__device__ __forceinline__ int prow32(int m) { return 4 * (m & 3) + ((m >> 2) & 3) + 16 * (m >> 4); }
+// (row + 16-byte unit) mod 16; permuting each group of 16 rows (even rows of
+// the group first, then odd) keeps both access patterns conflict-free: 16
+// lanes writing one 16-byte unit of 16 consecutive tile rows, and the
+// transposing reads of 8 consecutive tile rows x 32 bytes per 32 lanes.
+// Column offsets stay compile-time.
 __device__ __forceinline__ int prow16(int m) { return 2 * (m & 7) + (m >> 3); }
+__device__ __forceinline__ int prow32(int m) { return 16 * (m >> 4) + prow16(m & 15); }
 
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma16x32(u32x4 a, u32x4 b, f32x4 c) {
@@ -31,6 +32,25 @@ __device__ __forceinline__ f32x4 mfma16x32(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma16x16(u32x2 a, u32x2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4v, a),
                                                    __builtin_bit_cast(bf16x4v, b), c, 0, 0, 0);
+}
+
+// D += A.B on a 16x16x32 tile with D in VGPRs.  The products whose
+// accumulators live in the AGPR file (the self-conditioning sums fill all 256
+// of them) go through the builtin; the per-tile logits accumulate in VGPRs
+// through this form, so the register allocator never has to move
+// accumulators between the two files.  The compiler does not track the
+// hazards of inline assembly: the leading s_nop gives the 2 wait states a
+// product needs after a VALU write of any of its operands (the zeroed
+// accumulator at the start of a tile); a chain of these products on one
+// accumulator needs none; reads of the result by other instructions wait in
+// mfma_v_settle.
+__device__ __forceinline__ void mfma16x32_v(u32x4 a, u32x4 b, f32x4& d) {
+  asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+// Wait states between the last VGPR-form product and any other reader of its
+// result.
+__device__ __forceinline__ void mfma_v_settle(f32x4 (&lg)[2][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(lg[0][0]), "+v"(lg[0][1]), "+v"(lg[1][0]), "+v"(lg[1][1]));
 }
 
 // Workgroup -> (row block, vocab split).  Workgroups are dispatched round-robin
@@ -45,21 +65,27 @@ __device__ __forceinline__ void vocab_block(int nrb, int& rb, int& split) {
 
 // ---------------------------------------------------------------------------
 // Variant 32 (d = 4*SLICE <= 2048).  Workgroup = 4 waves, 32 rows of Z, one
-// vocab split; wave w owns the d-slice [w*SLICE, (w+1)*SLICE).
+// vocab split; wave w owns the d-slice [w*SLICE, (w+1)*SLICE).  Vocab tiles
+// hold 32 ids; every product is a 16x16x32 MFMA.  Lane l = 16 g + r.
 //
-// Per 32-id vocab tile, wave w computes the partial logits^T over its d-slice
-//   lg^T[v][row] = E[v, slice] . Z[row, slice]^T   (A = E rows from global,
-//                                                    B = Z fragments in VGPRs)
-// the 4 partials are summed through LDS (fixed order), every wave then runs
-// the same max / argmax / sum on the full logits, and accumulates its slice of
-//   S^T[slice][row] += E[tile, slice]^T . P^T       (A = E tile read back
-//                                                    transposed from LDS,
-//                                                    B = P in registers)
-// The E tile is staged in LDS by the same wave that loaded it (no barrier);
-// the product for tile t-1 is interleaved chunk by chunk with the logits of
-// tile t, and tile t's chunk c overwrites tile t-1's chunk c right after it
-// is consumed, so one tile of LDS per wave suffices.  Each lane owns one row
-// (row = lane % 32) in every layout, so the softmax state stays in-lane.
+// Per tile and 32-column chunk c of its slice, wave w accumulates the partial
+//   lg^T[v][row] += E[v, chunk] . Z[row, chunk]^T
+// over the 2 x 2 blocks (ids 16j.., rows 16h..) of the tile: A = E rows from
+// global, where one load instruction covers 16 ids x 64 contiguous bytes (a
+// 32-id operand would touch 32 rows x 32 bytes per instruction, which the
+// vector memory path serves several times slower); B = Z fragments in VGPRs.
+// The 4 partials are summed through LDS in a fixed order; every wave then
+// runs the same max / argmax / sum on the full logits and accumulates its
+// slice of
+//   S^T[col][row] += E[tile, col]^T . P^T   (A = the E tile read back
+//                                            transposed from LDS, B = P)
+// In the contraction over the 32 ids, k-slot 8g + 4j + i stands for id
+// 16j + 4g + i on both operands: the lane holding logit (row 16h + r, id
+// 16j + 4g + i) is then the lane whose P operand needs it, so P never leaves
+// registers.  The E tile is staged in LDS by the wave that loaded it (no
+// barrier); the product for tile t-1 is interleaved chunk by chunk with the
+// logits of tile t, and tile t's chunk c overwrites tile t-1's chunk c right
+// after the latter was read, so one tile of LDS per wave suffices.
 //
 // P = exp(l - m_seg) uses a reference m_seg per row that is fixed for a
 // "segment" of tiles; only when a logit exceeds it by more than kLazyTh does
@@ -70,208 +96,289 @@ __device__ __forceinline__ void vocab_block(int nrb, int& rb, int& split) {
 // Output: G (unnormalised, relative to m_G) and per-row (m_G, sum, max,
 // argmax) for the combine.
 // ---------------------------------------------------------------------------
+#ifndef DG_VOCAB32_PF
+#define DG_VOCAB32_PF 4
+#endif
+// Buffer resource over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_ld128(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+}
+
 template <int SLICE>
 __global__ void __launch_bounds__(256, 1)
     k_vocab32(const u16* __restrict__ Z, const u16* __restrict__ E, int R, int d, int V, int nrb,
               int split_len, float* __restrict__ pS, f32x4* __restrict__ pstat) {
-  constexpr int NCH = SLICE / 32, KSN = SLICE / 16, EP = SLICE + 8;
-  constexpr int PF = NCH < 4 ? NCH : (SLICE >= 512 ? 2 : 4);  // chunks of E in flight
+  constexpr int NCH = SLICE / 32, EP = SLICE + 8;
+  constexpr int PF = NCH < DG_VOCAB32_PF ? NCH : DG_VOCAB32_PF;  // chunks of E in flight
+  // chunk c of every tile lives in ring slot c % PF, which needs PF | NCH
+  static_assert(NCH % PF == 0, "the prefetch depth must divide the chunks per tile");
   __shared__ __attribute__((aligned(16))) u16 Et[4][32][EP];
-  __shared__ __attribute__((aligned(16))) f32x4 xch[4][4][64];  // [wave][16-byte chunk][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 xch[4][4][64];  // [wave][block 2j+h][rotated lane]
+  __shared__ __attribute__((aligned(16))) u32x4 Pbuf[2][4][16];  // P of row 16h + r, slots 8g..8g+7
+  __shared__ float Sbuf[32];                                    // per-row fold factor
+  __shared__ int flags[4];
 
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, l32 = l & 31;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, r = l & 15;
   int rb, split;
   vocab_block(nrb, rb, split);
   const int r0 = rb * 32;
   const int vs = split * split_len, ve = min(V, vs + split_len);
   const int dbase = w * SLICE;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
-
-  const int zr = r0 + l32;
-  const bool zok = zr < R;
-  // Rows past R load a copy of row R-1 (branch-free); their results are never stored.
-  u32x4 zf[KSN];
-  {
-    const u16* zp = Z + (size_t)(zok ? zr : R - 1) * d + dbase + h * 8;
-#pragma unroll
-    for (int ks = 0; ks < KSN; ++ks) zf[ks] = ldg128(zp + ks * 16);
-  }
-  float* gp = pS + ((size_t)split * R + (zok ? zr : 0)) * d + dbase + 4 * h;
   const size_t tofs = (size_t)gridDim.x / nrb * R * d;  // temp area follows the nsplit partials
+
+  // Rows 16h + r of the block.  Rows past R load a copy of row R-1
+  // (branch-free); their results are never stored.
+  u32x4 zf[2][NCH];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int zr = min(r0 + 16 * h + r, R - 1);
+    const u16* zp = Z + (size_t)zr * d + dbase + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) zf[h][c] = ldg128(zp + 32 * c);
+  }
+
   DG_LDS u16* et = (DG_LDS u16*)&Et[w][0][0];
   const int nt = ve > vs ? (ve - vs + 31) / 32 : 0;
   for (int e = l * 8; e < 32 * EP; e += 64 * 8) *(DG_LDS u32x4*)(et + e) = z4;
-  // transposing-read addresses of this lane: tile rows tr_r + {0, 8, 16, 24},
-  // column 16*((l>>4)&1) + 4*(l&3) inside each 32-column chunk
-  const int tr_r = 4 * h + ((l & 15) >> 2);
-  const int tr_c = 16 * ((l >> 4) & 1) + (l & 3) * 4;
-  const DG_LDS u16* trb[4];
+  // this lane's LDS addresses: the 16 bytes it loaded of ids 16j + r, and the
+  // transposing reads of ids 16j + 4g + (0..3) at column r of a 16-column block
+  DG_LDS u16* wrb[2];
+  const DG_LDS u16* trb[2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) trb[s] = et + prow32(tr_r + 8 * s) * EP + tr_c;
-  DG_LDS u16* wrb = et + prow32(l32) * EP + h * 8;
+  for (int j = 0; j < 2; ++j) {
+    wrb[j] = et + prow32(16 * j + r) * EP + 8 * g;
+    trb[j] = et + prow32(16 * j + 4 * g + (r >> 2)) * EP + 4 * (r & 3);
+  }
 
   // E fragments of chunk c (columns [32c, 32c+32) of the slice) of a tile live
-  // in ring slot c % PF; they are issued PF chunks ahead of their use.
-  u32x4 ring0[PF], ring1[PF];
-  // Ids past the split or V load a copy of row V-1 (branch-free): their logits
-  // are masked to -inf, so their probabilities are exactly 0.
+  // in ring slot c % PF; they are issued PF chunks ahead of their use.  E is
+  // the tiled table: the 16 B this lane needs (id 16j + r, columns 8g..8g+7
+  // of the chunk) sit at lane position l of a contiguous 1 KiB block, so
+  // each load instruction reads one block.  The buffer resource ends at the
+  // table's end: ids past it read zeros, and ids past the split are masked to
+  // -inf below, so their probabilities are exactly 0.
+  const uint32_t blk_row = (uint32_t)d * 32u;  // bytes of the d/32 blocks of 16 ids
+  const __amdgpu_buffer_rsrc_t erc = buffer_rsrc(E, (uint32_t)(((size_t)V + 15) / 16 * blk_row));
+  const uint32_t lane_off = (uint32_t)((size_t)(vs / 16) * blk_row + (size_t)(w * NCH) * 1024u + l * 16u);
+  u32x4 ring0[PF], ring1[PF];  // ids 16j + r, j = 0, 1
   auto issue = [&](int slot, int tile, int c) {
-    const int ev = min(vs + tile * 32 + l32, V - 1);
-    const u16* ep = E + (size_t)ev * d + dbase + h * 8 + c * 32;
-    ring0[slot] = ldg128(ep);
-    ring1[slot] = ldg128(ep + 16);
+    const uint32_t o = lane_off + (uint32_t)tile * (2u * blk_row) + 1024u * c;
+    ring0[slot] = buffer_ld128(erc, o);
+    ring1[slot] = buffer_ld128(erc, o + blk_row);
   };
 #pragma unroll
   for (int c = 0; c < PF; ++c) issue(c, 0, c);
 
-  float m_seg = -INFINITY, lsum = 0.f;        // current segment
-  float m_G = -INFINITY, l_G = 0.f;           // folded partial
-  bool g_valid = false;
-  float m_true = -INFINITY, tmax = -INFINITY;
-  int amax = 0;
-  u32x4 pf0 = z4, pf1 = z4;
-
-  // full logits of the current tile from the exchange buffer (fixed order)
-  auto gather_logits = [&](int v0, float* L) {
+  // A operands of the P.E product of one chunk, columns 16kb..16kb+15
+  u32x4 tra[2];
+  auto tr_load = [&](int c) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 a = xch[0][q][l];
-      a += xch[1][q][l];
-      a += xch[2][q][l];
-      a += xch[3][q][l];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = v0 + 8 * q + 4 * h + i;  // element 4q+i is id v0 + 8q + 4h + i
-        L[4 * q + i] = v < ve ? a[i] : -INFINITY;
-      }
+    for (int kb = 0; kb < 2; ++kb) {
+      const u32x2 a = lds_read_tr16(trb[0] + 32 * c + 16 * kb);
+      const u32x2 b = lds_read_tr16(trb[1] + 32 * c + 16 * kb);
+      tra[kb] = u32x4{a[0], a[1], b[0], b[1]};
     }
   };
-  auto make_p = [&](const float* L) {
-    float pv[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      // the normaliser sums the fp32 probabilities; bf16 copies feed P.E
-      pv[e] = L[e] == -INFINITY ? 0.f : exp2f((L[e] - m_seg) * kLog2e);
-      lsum += pv[e];
-    }
-    pf0 = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                pack_bf16x2(pv[6], pv[7])};
-    pf1 = u32x4{pack_bf16x2(pv[8], pv[9]), pack_bf16x2(pv[10], pv[11]),
-                pack_bf16x2(pv[12], pv[13]), pack_bf16x2(pv[14], pv[15])};
+  tr_load(0);  // zeros: the first tile's product adds 0 * 0
+
+  // ---- softmax bookkeeping: each wave owns 8 rows ----------------------------
+  // After the 4 d-slice partials of a tile are exchanged, wave w sums them
+  // for rows 16 ho + 8 (w & 1) + rho only (ho = w >> 1), lane 8 rho + 4 oj +
+  // og taking ids 16 oj + 4 og + (0..3) of row rho, and keeps that row's
+  // reference m_seg, running max / first argmax and its part of the running
+  // sum.  It writes P of its rows (bf16, in the order of the P.E operand) and
+  // the row's fold factor to LDS; after a barrier every wave reads the whole
+  // P tile.  The partials sit in the exchange buffer at a lane position
+  // rotated by (2g + 8j), which keeps both the writes and the owners' reads
+  // free of bank conflicts.
+  const int ho = w >> 1, rho = l >> 3, oj = (l >> 2) & 1, og = l & 3;
+  const int orow = 8 * (w & 1) + rho;  // owned row within its 16-row half
+  float m_seg = -INFINITY, lsum = 0.f, m_true = -INFINITY;
+  int amax = 0;
+  bool g_valid = false;
+  u32x4 pf[2] = {z4, z4};
+
+  // max with the lowest id on ties, over the 8 lanes of a row (DPP: swap
+  // neighbours, swap pairs, mirror the two quads)
+  auto row_argmax = [](float& m, int& a) {
+    auto step = [&](float om, int oa) {
+      const bool take = om > m || (om == m && oa < a);
+      m = take ? om : m;
+      a = take ? oa : a;
+    };
+    step(__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)),
+         __builtin_amdgcn_update_dpp(0, a, 0xB1, 0xF, 0xF, false));
+    step(__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)),
+         __builtin_amdgcn_update_dpp(0, a, 0x4E, 0xF, 0xF, false));
+    step(__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)),
+         __builtin_amdgcn_update_dpp(0, a, 0x141, 0xF, 0xF, false));
+  };
+  auto row_sum = [](float s) {
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x141, 0xF, 0xF, false));
+    return s;
   };
 
   int t = 0;
   for (;;) {  // segments
-    f32x16 acc[NCH];
+    f32x4 acc[NCH][2][2];  // [chunk][kb][h]
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) acc[c] = zero16();
-    bool rescale = false;
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[c][k >> 1][k & 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool fold_now = false;
     for (;; ++t) {  // tiles
       const bool have = t < nt;
-      f32x16 lg = zero16();
+      f32x4 lg[2][2];  // [j][h]
+#pragma unroll
+      for (int k = 0; k < 4; ++k) lg[k >> 1][k & 1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int slot = c % PF;
         // Branch-free body: on the first tile P = 0 and the LDS tile is zero;
         // on the drain pass (t == nt) the logits are computed and discarded.
         const u32x4 e0 = ring0[slot], e1 = ring1[slot];
-        lg = mfma32(e0, zf[2 * c], lg);
-        lg = mfma32(e1, zf[2 * c + 1], lg);
+        mfma16x32_v(e0, zf[0][c], lg[0][0]);
+        mfma16x32_v(e0, zf[1][c], lg[0][1]);
+        mfma16x32_v(e1, zf[0][c], lg[1][0]);
+        mfma16x32_v(e1, zf[1][c], lg[1][1]);
+        // the transposed E of this chunk (tile t-1) was read during the
+        // previous chunk
+        acc[c][0][0] = mfma16x32(tra[0], pf[0], acc[c][0][0]);
+        acc[c][0][1] = mfma16x32(tra[0], pf[1], acc[c][0][1]);
+        acc[c][1][0] = mfma16x32(tra[1], pf[0], acc[c][1][0]);
+        acc[c][1][1] = mfma16x32(tra[1], pf[1], acc[c][1][1]);
+        // read the next chunk of tile t-1 (chunk c+1 is only overwritten in
+        // the next chunk, after this read)
+        if (c + 1 < NCH) tr_load(c + 1);
+        // 8-byte LDS writes run at twice the rate of 16-byte ones; lanes of
+        // odd g write their upper half first so that the 32 lanes of each
+        // half-wave cover all 64 banks
+        {
+          const bool odd = g & 1;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const u32x2 a0 = lds_read_tr16(trb[2 * p] + c * 32);
-          const u32x2 a1 = lds_read_tr16(trb[2 * p + 1] + c * 32);
-          acc[c] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, p ? pf1 : pf0, acc[c]);
+          for (int j = 0; j < 2; ++j) {
+            const u32x4 e = j ? e1 : e0;
+            const u32x2 lo = {e[0], e[1]}, hi = {e[2], e[3]};
+            DG_LDS u16* wp = wrb[j] + 32 * c;
+            *(DG_LDS u32x2*)(wp + (odd ? 4 : 0)) = odd ? hi : lo;
+            *(DG_LDS u32x2*)(wp + (odd ? 0 : 4)) = odd ? lo : hi;
+          }
         }
-        *(DG_LDS u32x4*)(wrb + c * 32) = e0;
-        *(DG_LDS u32x4*)(wrb + c * 32 + 16) = e1;
         if (c + PF < NCH)
           issue(slot, t, c + PF);
         else
           issue(slot, t + 1, c + PF - NCH);
         __builtin_amdgcn_sched_barrier(0);
       }
+      tr_load(0);  // chunk 0 of this tile, for the next tile's P.E
+      mfma_v_settle(lg);
       if (!have) break;
 
-      // sum the four d-slice partials
+      // exchange the d-slice partials
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        xch[w][q][l] = f32x4{lg[4 * q], lg[4 * q + 1], lg[4 * q + 2], lg[4 * q + 3]};
+      for (int k = 0; k < 4; ++k) {
+        const int j = k >> 1, h = k & 1;
+        xch[w][k][16 * g + ((r + 2 * g + 8 * j) & 15)] = lg[j][h];
+      }
       __syncthreads();
       const int v0 = vs + t * 32;
-      float L[16];
-      gather_logits(v0, L);
-      __syncthreads();
-
-      tmax = -INFINITY;
-      int targ = 0x7fffffff;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int v = v0 + 8 * (e >> 2) + 4 * h + (e & 3);
-        const bool gt = L[e] > tmax;  // ids increase with e: the first maximum is kept
-        tmax = gt ? L[e] : tmax;
-        targ = gt ? v : targ;
-      }
       {
-        const float om = __shfl_xor(tmax, 32);
-        const int oa = __shfl_xor(targ, 32);
-        const bool take = om > tmax || (om == tmax && oa < targ);
-        tmax = take ? om : tmax;
-        targ = take ? oa : targ;
+        const int pos = 16 * og + ((orow + 2 * og + 8 * oj) & 15), blk = 2 * oj + ho;
+        f32x4 a = xch[0][blk][pos];
+        a += xch[1][blk][pos];
+        a += xch[2][blk][pos];
+        a += xch[3][blk][pos];
+        const int id0 = v0 + 16 * oj + 4 * og;
+        float x[4], tm = -INFINITY;
+        int ta = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = id0 + i < ve ? a[i] : -INFINITY;
+          const bool gt = x[i] > tm;  // ids increase with i: the first maximum is kept
+          tm = gt ? x[i] : tm;
+          ta = gt ? id0 + i : ta;
+        }
+        row_argmax(tm, ta);
+        amax = tm > m_true ? ta : amax;  // earlier tiles win ties
+        m_true = fmaxf(m_true, tm);
+        // Lazy reference: it only moves when a logit exceeds it by more than
+        // kLazyTh; the accumulated sums are then rescaled by s = e^(m_old - m_new).
+        float s = 1.f;
+        if (m_seg == -INFINITY) {
+          m_seg = tm;  // first tile of the split
+        } else if (tm > m_seg + kLazyTh) {
+          s = exp2f((m_seg - tm) * kLog2e);
+          lsum *= s;
+          m_seg = tm;
+        }
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // the normaliser sums the fp32 probabilities; bf16 copies feed P.E
+          p[i] = x[i] == -INFINITY ? 0.f : exp2f((x[i] - m_seg) * kLog2e);
+          lsum += p[i];
+        }
+        *(DG_LDS u32x2*)((DG_LDS char*)&Pbuf[ho][og][orow] + 8 * oj) =
+            u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+        if ((l & 7) == 0) Sbuf[16 * ho + orow] = s;
+        const bool need = __any(s != 1.f);
+        if (l == 0) flags[w] = need ? 1 : 0;
       }
-      amax = tmax > m_true ? targ : amax;  // earlier tiles win ties
-      m_true = fmaxf(m_true, tmax);
-      if (m_seg == -INFINITY) {
-        m_seg = tmax;  // first tile of the split
-      } else if (__any(tmax > m_seg + kLazyTh)) {
-        rescale = true;  // fold and restart before this tile's P
+      __syncthreads();
+      pf[0] = Pbuf[0][g][r];
+      pf[1] = Pbuf[1][g][r];
+      if (flags[0] | flags[1] | flags[2] | flags[3]) {
+        fold_now = true;  // fold before this tile's P.E
         break;
       }
-      make_p(L);
     }
 
-    // Fold the segment into G.  The accumulator is only ever stored raw (never
-    // touched by VALU code, so it stays in AGPRs): the first fold makes it G
-    // (reference m_seg); a later fold stores it to the temp area T and merges
-    // G = G e^(m_G - m) + T e^(m_seg - m) with plain loads and stores.
-    const float m_new = rescale ? fmaxf(m_seg, tmax) : m_seg;
-    float* dst = g_valid ? gp + tofs : gp;
-    if (zok) {
-#pragma unroll
-      for (int c = 0; c < NCH; ++c)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *(f32x4*)(dst + 32 * c + 8 * j) =
-              f32x4{acc[c][4 * j], acc[c][4 * j + 1], acc[c][4 * j + 2], acc[c][4 * j + 3]};
+    // Fold the segment into G with the per-row factor s: G = (G + acc) s
+    // (G = acc s on the first fold; s = 1 at the end of the split).  The
+    // accumulator is only ever stored raw (never touched by VALU code, so it
+    // stays in AGPRs): the first fold stores it to G, a later one to the temp
+    // area T, which is then merged with plain loads and stores.
+    float s2[2] = {1.f, 1.f};
+    if (fold_now) {
+      s2[0] = Sbuf[r];
+      s2[1] = Sbuf[16 + r];
     }
-    if (!g_valid) {
-      m_G = m_seg;
-      l_G = lsum;
-      g_valid = true;
-    } else {
-      const float gs = m_G == -INFINITY ? 0.f : exp2f((m_G - m_new) * kLog2e);
-      const float as = m_seg == -INFINITY ? 0.f : exp2f((m_seg - m_new) * kLog2e);
-      if (zok) {
+    const bool merge = g_valid || fold_now;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int zr = r0 + 16 * h + r;
+      if (zr < R) {
+        float* gp = pS + ((size_t)split * R + zr) * d + dbase + 4 * g;
+        float* dst = g_valid ? gp + tofs : gp;
+#pragma unroll
         for (int c = 0; c < NCH; ++c)
-          for (int j = 0; j < 4; ++j) {
-            float* g = gp + 32 * c + 8 * j;
-            *(f32x4*)g = *(const f32x4*)g * gs + *(const f32x4*)(g + tofs) * as;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) *(f32x4*)(dst + 32 * c + 16 * kb) = acc[c][kb][h];
+        if (merge) {
+          for (int c = 0; c < 2 * NCH; ++c) {
+            float* q = gp + 16 * c;
+            f32x4 v = *(const f32x4*)q;
+            if (g_valid) v += *(const f32x4*)(q + tofs);
+            *(f32x4*)q = v * s2[h];
           }
+        }
       }
-      l_G = l_G * gs + lsum * as;
-      m_G = m_new;
     }
-    if (!rescale) break;
-    m_seg = m_new;
-    lsum = 0.f;
-    float L[16];
-    gather_logits(vs + t * 32, L);  // the exchange buffer still holds tile t
-    make_p(L);
+    g_valid = true;
+    if (!fold_now) break;
     ++t;
   }
 
-  l_G += __shfl_xor(l_G, 32);
-  if (zok && w == 0 && h == 0) pstat[(size_t)split * R + zr] = f32x4{m_G, l_G, m_true, __int_as_float(amax)};
+  const float tot = row_sum(lsum);
+  const int zr = r0 + 16 * ho + orow;
+  if (zr < R && (l & 7) == 0)
+    pstat[(size_t)split * R + zr] = f32x4{m_seg, tot, m_true, __int_as_float(amax)};
 }
 
 // ---------------------------------------------------------------------------
@@ -314,10 +421,14 @@ __global__ void __launch_bounds__(256, 1)
   const DG_LDS u16* trb = et + prow16(tr_r) * EP + (l & 3) * 4;
   DG_LDS u16* wrb = et + prow16(l16) * EP + g4 * 8;
 
+  // E is the tiled table (one 1 KiB block of 16 ids x 32 columns per load
+  // instruction, in operand lane order); ids past the table read zeros
+  const uint32_t blk_row = (uint32_t)d * 32u;
+  const __amdgpu_buffer_rsrc_t erc = buffer_rsrc(E, (uint32_t)(((size_t)V + 15) / 16 * blk_row));
+  const uint32_t lane_off = (uint32_t)((size_t)(vs / 16) * blk_row + (size_t)(dbase / 32) * 1024u + l * 16u);
   u32x4 ring0[PF];
   auto issue = [&](int slot, int tile, int c) {
-    const int ev = min(vs + tile * 16 + l16, V - 1);
-    ring0[slot] = ldg128(E + (size_t)ev * d + dbase + g4 * 8 + c * 32);
+    ring0[slot] = buffer_ld128(erc, lane_off + (uint32_t)tile * blk_row + 1024u * c);
   };
 #pragma unroll
   for (int c = 0; c < PF; ++c) issue(c, 0, c);
@@ -327,6 +438,7 @@ __global__ void __launch_bounds__(256, 1)
   float m_true = -INFINITY, tmax = -INFINITY;
   int amax = 0;
   u32x2 pf = {0u, 0u};
+  float L[4];  // logits of ids v0 + 4*g4 + i of the current tile
 
   auto gather_logits = [&](int v0, float* L) {
     f32x4 a = xch[0][l];
@@ -377,7 +489,6 @@ __global__ void __launch_bounds__(256, 1)
       xch[w][l] = lg;
       __syncthreads();
       const int v0 = vs + t * 16;
-      float L[4];
       gather_logits(v0, L);
       __syncthreads();
 
@@ -433,9 +544,7 @@ __global__ void __launch_bounds__(256, 1)
     if (!rescale) break;
     m_seg = m_new;
     lsum = 0.f;
-    float L[4];
-    gather_logits(vs + t * 16, L);
-    make_p(L);
+    make_p(L);  // this tile's P against the new reference (L still holds it)
     ++t;
   }
 
@@ -577,6 +686,31 @@ __global__ void __launch_bounds__(256) k_vocab_f32(int R, int d, int V, const fl
     conf[r] = (float)(1.0 / lsum);
     if (lse) lse[r] = (float)(m + log(lsum));
   }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled table: thread q writes 16 bytes of block q / 64 at lane position
+// q % 64 = 16 g + r: id 16 vb + r, columns 32 c + 8 g .. +7, where the block
+// is (vb, c) = (q / 64 / (d/32), q / 64 % (d/32)); ids past V are zero.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_pack_embedding(int V, int d, size_t n16, const u16* __restrict__ E,
+                                                        u32x4* __restrict__ out) {
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= n16) return;
+  const size_t b = q >> 6;
+  const int lane = (int)(q & 63), g = lane >> 4, r = lane & 15;
+  const size_t cpb = (size_t)d / 32;
+  const size_t vb = b / cpb, c = b % cpb;
+  const size_t id = vb * 16 + r;
+  out[q] = id < (size_t)V ? ldg128(E + id * d + c * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_pack_embedding(int V, int d, const void* E, void* E_tiled, hipStream_t s) {
+  const size_t n16 = ((size_t)V + 15) / 16 * 16 * (size_t)d / 8;
+  const size_t nb = (n16 + 255) / 256;
+  hipLaunchKernelGGL(k_pack_embedding, dim3((unsigned)nb), dim3(256), 0, s, V, d, n16, (const u16*)E,
+                     (u32x4*)E_tiled);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
