@@ -135,8 +135,9 @@ int dg_attn_bidir(const dg_dims *dims, const void *q, const void *k_cache, const
 /* Tiled layout of a bf16 embedding table for the vocabulary head.  E[V][d]
  * (row-major) is cut into blocks of 16 ids x 32 columns; block (vb, c) is
  * 1 KiB at byte offset (vb * (d / 32) + c) * 1024, and inside it entry
- * (id 16 vb + r, column 32 c + 8 g + e) sits at element 8 (16 g + r) + e
- * (g < 4, r < 16, e < 8).  Ids in [V, 16 ceil(V/16)) read as zero.  The
+ * (id 16 vb + r, column 32 c + 8 g + e) sits at element 8 (16 g + r) + e'
+ * with e' = e for even g and e' = e ^ 4 for odd g (g < 4, r < 16, e < 8).
+ * Ids in [V, 16 ceil(V/16)) read as zero.  The
  * vocabulary kernels load one block per instruction, 1 KiB contiguous, in
  * the lane order of their matrix-core operands.  Needs d % 32 == 0.
  * dg_tiled_embedding_bytes returns 16 ceil(V/16) d 2 (0 for invalid sizes or

@@ -80,8 +80,9 @@ def _run_vocab(R, d, V, E, Z, dtype):
 
 @pytest.mark.parametrize("V,d", [(37, 64), (3000, 256), (16, 4096)])
 def test_tiled_embedding_layout(V, d):
-    """The tiled table holds, at element 8(16g + r) + e of 1 KiB block
-    (vb, c), entry (16 vb + r, 32 c + 8 g + e) of E, zero past V."""
+    """The tiled table holds, at element 8(16g + r) + e' of 1 KiB block
+    (vb, c), entry (16 vb + r, 32 c + 8 g + e) of E (e' = e for even g,
+    e ^ 4 for odd g), zero past V."""
     import uniform_state_discrete_amd as dg
     say(f"tiled embedding V={V} d={d}")
     r = np.random.default_rng(V + d)
@@ -92,8 +93,10 @@ def test_tiled_embedding_layout(V, d):
     Vp = -(-V // 16) * 16
     ref = np.zeros((Vp, d), dtype=np.uint16)
     ref[:V] = E
-    # blocks [vb][c][g][r][e] <- ref[16 vb + r][32 c + 8 g + e]
-    ref = ref.reshape(Vp // 16, 16, d // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    # blocks [vb][c][g][r][e'] <- ref[16 vb + r][32 c + 8 g + e]
+    blk = ref.reshape(Vp // 16, 16, d // 32, 4, 8).transpose(0, 2, 3, 1, 4).copy()
+    blk[:, :, 1::2] = np.concatenate([blk[:, :, 1::2, :, 4:], blk[:, :, 1::2, :, :4]], axis=-1)
+    ref = blk.reshape(-1)
     assert np.array_equal(got, ref)
 
 

@@ -22,7 +22,6 @@ constexpr float kLazyTh = 40.0f;
 // transposing reads of 8 consecutive tile rows x 32 bytes per 32 lanes.
 // Column offsets stay compile-time.
 __device__ __forceinline__ int prow16(int m) { return 2 * (m & 7) + (m >> 3); }
-__device__ __forceinline__ int prow32(int m) { return 16 * (m >> 4) + prow16(m & 15); }
 
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma16x32(u32x4 a, u32x4 b, f32x4 c) {
@@ -52,6 +51,19 @@ __device__ __forceinline__ void mfma16x32_v(u32x4 a, u32x4 b, f32x4& d) {
 __device__ __forceinline__ void mfma_v_settle(f32x4 (&lg)[2][2]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(lg[0][0]), "+v"(lg[0][1]), "+v"(lg[1][0]), "+v"(lg[1][1]));
 }
+__device__ __forceinline__ void mfma_v_settle(f32x4& a, f32x4& b) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
+}
+
+// The tiled table stores the 16 bytes of a lane with odd g (columns
+// 8g..8g+7 of a chunk) as columns 8g+4..8g+7 then 8g..8g+3: those lanes
+// write their first 8 bytes to LDS column 8g+4, the others to 8g, so each
+// LDS store instruction covers all 64 banks without selecting data.  The
+// matrix-core contraction sees the same permuted k-slots on both operands:
+// the Z fragments of odd-g lanes get their halves swapped once, at load.
+__device__ __forceinline__ u32x4 swap_halves(u32x4 v, bool sw) {
+  return sw ? u32x4{v[2], v[3], v[0], v[1]} : v;
+}
 
 // Workgroup -> (row block, vocab split).  Workgroups are dispatched round-robin
 // over the 8 XCDs (blockIdx % 8); consecutive linear ids are given to one XCD,
@@ -66,38 +78,38 @@ __device__ __forceinline__ void vocab_block(int nrb, int& rb, int& split) {
 // ---------------------------------------------------------------------------
 // Variant 32 (d = 4*SLICE <= 2048).  Workgroup = 4 waves, 32 rows of Z, one
 // vocab split; wave w owns the d-slice [w*SLICE, (w+1)*SLICE).  Vocab tiles
-// hold 32 ids; every product is a 16x16x32 MFMA.  Lane l = 16 g + r.
+// hold 16 ids, and three tiles are in flight: iteration t computes the
+// logits of tile t, the softmax of tile t-1 and the self-conditioning
+// product of tile t-2, so the softmax work runs between the matrix-core
+// instructions instead of stalling them.  Lane l = 16 g + r.
 //
 // Per tile and 32-column chunk c of its slice, wave w accumulates the partial
-//   lg^T[v][row] += E[v, chunk] . Z[row, chunk]^T
-// over the 2 x 2 blocks (ids 16j.., rows 16h..) of the tile: A = E rows from
-// global, where one load instruction covers 16 ids x 64 contiguous bytes (a
-// 32-id operand would touch 32 rows x 32 bytes per instruction, which the
-// vector memory path serves several times slower); B = Z fragments in VGPRs.
-// The 4 partials are summed through LDS in a fixed order; every wave then
-// runs the same max / argmax / sum on the full logits and accumulates its
-// slice of
-//   S^T[col][row] += E[tile, col]^T . P^T   (A = the E tile read back
-//                                            transposed from LDS, B = P)
-// In the contraction over the 32 ids, k-slot 8g + 4j + i stands for id
-// 16j + 4g + i on both operands: the lane holding logit (row 16h + r, id
-// 16j + 4g + i) is then the lane whose P operand needs it, so P never leaves
-// registers.  The E tile is staged in LDS by the wave that loaded it (no
-// barrier); the product for tile t-1 is interleaved chunk by chunk with the
-// logits of tile t, and tile t's chunk c overwrites tile t-1's chunk c right
-// after the latter was read, so one tile of LDS per wave suffices.
+//   lg^T[v][row] += E[v, chunk] . Z[row, chunk]^T        (16x16x32, rows 16h..)
+// with A = one block of the tiled E (16 ids x 32 columns, 1 KiB read by one
+// load instruction) and B = Z fragments in VGPRs.  The block is also written
+// to LDS (buffer t & 1, over tile t-2's data right after it was read) and
+// later read back transposed for
+//   S^T[col][row] += E[tile, col]^T . P^T                (32x32x16)
+// whose B operand, P^T, comes from an LDS tile that the softmax step writes in
+// operand order.
 //
-// P = exp(l - m_seg) uses a reference m_seg per row that is fixed for a
-// "segment" of tiles; only when a logit exceeds it by more than kLazyTh does
-// the segment end: the accumulator is folded into the split's partial in
-// global memory, G = G e^(m_G - m) + acc e^(m_seg - m), and a new segment
-// starts from a zero accumulator.  The accumulator is therefore never
-// rescaled inside the tile loop (it stays in the AGPR file).
-// Output: G (unnormalised, relative to m_G) and per-row (m_G, sum, max,
-// argmax) for the combine.
+// Softmax of a tile: the four d-slice partials are exchanged through LDS (at
+// rotated lane positions: conflict-free); wave w owns rows 8w..8w+7, sums
+// their partials (lane 8 rho + q: ids 2q, 2q+1 of row 8w + rho), reduces max /
+// first argmax over the 8 lanes of a row with DPP, keeps the row's reference
+// m_seg, running max / argmax and part of the running sum, and writes P
+// (bf16) and the row's fold factor to LDS.
+//
+// P = exp(l - m_seg) uses a reference that only moves when a logit exceeds it
+// by more than kLazyTh; then s = e^(m_old - m_new) rescales the running sum
+// at once and, after the product of the tile before has been accumulated,
+// every wave folds its accumulator into the split's partial in global memory,
+// G = (G + acc) s, and starts a zero accumulator (the accumulator is only
+// ever stored raw, so it stays in the AGPR file).  Output: G (unnormalised,
+// relative to the final m_seg) and per-row (m_seg, sum, max, argmax).
 // ---------------------------------------------------------------------------
 #ifndef DG_VOCAB32_PF
-#define DG_VOCAB32_PF 4
+#define DG_VOCAB32_PF 8
 #endif
 // Buffer resource over [base, base + bytes): loads past the end return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
@@ -105,6 +117,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 __device__ __forceinline__ u32x4 buffer_ld128(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+}
+// LDS row of a 16-row tile row m: the 16-lane writes of one 16-byte unit of 16
+// consecutive rows and the transposing reads of 4 rows x 4 units per 32 lanes
+// fall on distinct banks (rows are padded by 16 bytes).
+__device__ __forceinline__ int prow16t(int m) { return 4 * (m & 3) + (m >> 2); }
+// max with the lowest id on ties, and sums, over 8 consecutive lanes (DPP:
+// swap neighbours, swap pairs, mirror the two quads)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& m, int& a) {
+  const float om = dpp_f<CTRL>(m);
+  const int oa = dpp_i<CTRL>(a);
+  const bool take = (om > m) | ((om == m) & (oa < a));  // branch-free
+  m = take ? om : m;
+  a = take ? oa : a;
+}
+__device__ __forceinline__ float sum8(float s) {
+  s += dpp_f<0xB1>(s);
+  s += dpp_f<0x4E>(s);
+  s += dpp_f<0x141>(s);
+  return s;
 }
 
 template <int SLICE>
@@ -115,13 +155,23 @@ __global__ void __launch_bounds__(256, 1)
   constexpr int PF = NCH < DG_VOCAB32_PF ? NCH : DG_VOCAB32_PF;  // chunks of E in flight
   // chunk c of every tile lives in ring slot c % PF, which needs PF | NCH
   static_assert(NCH % PF == 0, "the prefetch depth must divide the chunks per tile");
-  __shared__ __attribute__((aligned(16))) u16 Et[4][32][EP];
-  __shared__ __attribute__((aligned(16))) f32x4 xch[4][4][64];  // [wave][block 2j+h][rotated lane]
-  __shared__ __attribute__((aligned(16))) u32x4 Pbuf[2][4][16];  // P of row 16h + r, slots 8g..8g+7
-  __shared__ float Sbuf[32];                                    // per-row fold factor
-  __shared__ int flags[4];
+  // chunks at which the softmax steps of the previous tile run: every LDS
+  // result is consumed two chunks after it was requested, so its latency
+  // hides behind matrix-core work instead of stalling the wave's issue
+  constexpr int kRdX = 0;                      // request the partials
+  constexpr int kSum = NCH > 2 ? 2 : NCH - 1;  // sum them, first reductions
+  constexpr int kRed = NCH > 3 ? 3 : NCH - 1;  // finish max / argmax
+  constexpr int kExp = NCH > 4 ? 4 : NCH - 1;  // reference, P, fold factor
+  __shared__ __attribute__((aligned(16))) u16 Et[2][4][16][EP];
+  // softmax exchange buffers, double-buffered by tile parity so that one
+  // barrier per iteration suffices
+  __shared__ __attribute__((aligned(16))) f32x4 xch[2][4][2][64];  // [tile & 1][wave][h][rotated lane]
+  __shared__ __attribute__((aligned(16))) u32x4 Pbuf[2][2][32];     // [tile & 1]: P of row m, ids 8k..8k+7
+  __shared__ float Sbuf[2][32];                                     // [tile & 1]: per-row fold factor
+  __shared__ int flags[2][4];
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, r = l & 15;
+  const int h2 = l >> 5, m32 = l & 31;
   int rb, split;
   vocab_block(nrb, rb, split);
   const int r0 = rb * 32;
@@ -135,250 +185,219 @@ __global__ void __launch_bounds__(256, 1)
   u32x4 zf[2][NCH];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int zr = min(r0 + 16 * h + r, R - 1);
-    const u16* zp = Z + (size_t)zr * d + dbase + 8 * g;
+    const u16* zp = Z + (size_t)min(r0 + 16 * h + r, R - 1) * d + dbase + 8 * g;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) zf[h][c] = ldg128(zp + 32 * c);
+    for (int c = 0; c < NCH; ++c) zf[h][c] = swap_halves(ldg128(zp + 32 * c), g & 1);
   }
 
-  DG_LDS u16* et = (DG_LDS u16*)&Et[w][0][0];
-  const int nt = ve > vs ? (ve - vs + 31) / 32 : 0;
-  for (int e = l * 8; e < 32 * EP; e += 64 * 8) *(DG_LDS u32x4*)(et + e) = z4;
-  // this lane's LDS addresses: the 16 bytes it loaded of ids 16j + r, and the
-  // transposing reads of ids 16j + 4g + (0..3) at column r of a 16-column block
-  DG_LDS u16* wrb[2];
-  const DG_LDS u16* trb[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    wrb[j] = et + prow32(16 * j + r) * EP + 8 * g;
-    trb[j] = et + prow32(16 * j + 4 * g + (r >> 2)) * EP + 4 * (r & 3);
+  const int nt = ve > vs ? (ve - vs + 15) / 16 : 0;
+  // Tile order: the 8 row blocks of a split stream the same E tiles.  In
+  // lockstep every workgroup would wait the full HBM latency on every load,
+  // with only one workgroup's worth of distinct bytes in flight per split.
+  // Instead, within each round of 8 tiles, row block rb starts at tile
+  // (rb + s) % 8 of the round: the first step of a round fetches 8 tiles
+  // at once, the other 7 find their tiles in L2.  A last partial round goes
+  // in order.
+  const int nt8 = nt & ~7;
+  auto phys = [&](int s) { return s < nt8 ? (s & ~7) | ((s + rb) & 7) : s; };
+  {
+    DG_LDS u16* e0p = (DG_LDS u16*)&Et[0][w][0][0];
+    DG_LDS u16* e1p = (DG_LDS u16*)&Et[1][w][0][0];
+    for (int e = l * 8; e < 16 * EP; e += 64 * 8) {
+      *(DG_LDS u32x4*)(e0p + e) = z4;
+      *(DG_LDS u32x4*)(e1p + e) = z4;
+    }
   }
+  // this lane's LDS offsets (elements) inside a wave's tile: the 16 bytes it
+  // loaded (id r, columns 8g..8g+7 of a chunk), and the transposing reads of
+  // ids 8 h2 + 4k + (0..3) at column m32 of a chunk (k = 0, 1)
+  const int wr_a = prow16t(r) * EP + 8 * g + ((g & 1) ? 4 : 0), wr_b = wr_a ^ 4;
+  int tr_off[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    tr_off[k] = prow16t(8 * h2 + 4 * k + ((l & 15) >> 2)) * EP + 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
-  // E fragments of chunk c (columns [32c, 32c+32) of the slice) of a tile live
-  // in ring slot c % PF; they are issued PF chunks ahead of their use.  E is
-  // the tiled table: the 16 B this lane needs (id 16j + r, columns 8g..8g+7
-  // of the chunk) sit at lane position l of a contiguous 1 KiB block, so
-  // each load instruction reads one block.  The buffer resource ends at the
-  // table's end: ids past it read zeros, and ids past the split are masked to
-  // -inf below, so their probabilities are exactly 0.
+  // E blocks of chunk c live in ring slot c % PF, issued PF chunks ahead.
+  // E is the tiled table: the 16 bytes this lane needs sit at lane position l
+  // of a contiguous 1 KiB block.  The buffer resource ends at the table's end
+  // (ids past it read zeros); ids outside the split are masked to -inf.
   const uint32_t blk_row = (uint32_t)d * 32u;  // bytes of the d/32 blocks of 16 ids
   const __amdgpu_buffer_rsrc_t erc = buffer_rsrc(E, (uint32_t)(((size_t)V + 15) / 16 * blk_row));
   const uint32_t lane_off = (uint32_t)((size_t)(vs / 16) * blk_row + (size_t)(w * NCH) * 1024u + l * 16u);
-  u32x4 ring0[PF], ring1[PF];  // ids 16j + r, j = 0, 1
-  auto issue = [&](int slot, int tile, int c) {
-    const uint32_t o = lane_off + (uint32_t)tile * (2u * blk_row) + 1024u * c;
-    ring0[slot] = buffer_ld128(erc, o);
-    ring1[slot] = buffer_ld128(erc, o + blk_row);
+  u32x4 ring[PF];
+  auto issue = [&](int slot, int step, int c) {
+    ring[slot] = buffer_ld128(erc, lane_off + (uint32_t)phys(step) * blk_row + 1024u * c);
   };
 #pragma unroll
   for (int c = 0; c < PF; ++c) issue(c, 0, c);
 
-  // A operands of the P.E product of one chunk, columns 16kb..16kb+15
+  // A operands of the P.E product: ids 8 h2 .. 8 h2 + 7 at column m32 of a
+  // chunk; chunk c's sits in slot c & 1 and is read two chunks ahead
   u32x4 tra[2];
-  auto tr_load = [&](int c) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const u32x2 a = lds_read_tr16(trb[0] + 32 * c + 16 * kb);
-      const u32x2 b = lds_read_tr16(trb[1] + 32 * c + 16 * kb);
-      tra[kb] = u32x4{a[0], a[1], b[0], b[1]};
-    }
+  auto tr_load = [&](const DG_LDS u16* tile, int c, int slot) {
+    const u32x2 a = lds_read_tr16(tile + tr_off[0] + 32 * c);
+    const u32x2 b = lds_read_tr16(tile + tr_off[1] + 32 * c);
+    tra[slot] = u32x4{a[0], a[1], b[0], b[1]};
   };
-  tr_load(0);  // zeros: the first tile's product adds 0 * 0
+  // zeros: tile -2 adds 0 * 0
+  tr_load((const DG_LDS u16*)&Et[0][w][0][0], 0, 0);
+  tr_load((const DG_LDS u16*)&Et[0][w][0][0], NCH > 1 ? 1 : 0, 1);
 
-  // ---- softmax bookkeeping: each wave owns 8 rows ----------------------------
-  // After the 4 d-slice partials of a tile are exchanged, wave w sums them
-  // for rows 16 ho + 8 (w & 1) + rho only (ho = w >> 1), lane 8 rho + 4 oj +
-  // og taking ids 16 oj + 4 og + (0..3) of row rho, and keeps that row's
-  // reference m_seg, running max / first argmax and its part of the running
-  // sum.  It writes P of its rows (bf16, in the order of the P.E operand) and
-  // the row's fold factor to LDS; after a barrier every wave reads the whole
-  // P tile.  The partials sit in the exchange buffer at a lane position
-  // rotated by (2g + 8j), which keeps both the writes and the owners' reads
-  // free of bank conflicts.
-  const int ho = w >> 1, rho = l >> 3, oj = (l >> 2) & 1, og = l & 3;
-  const int orow = 8 * (w & 1) + rho;  // owned row within its 16-row half
+  // softmax state of the owned row 8w + rho (lane 8 rho + q holds ids 2q, 2q+1)
+  const int rho = l >> 3, q = l & 7, orow = 8 * w + rho;
   float m_seg = -INFINITY, lsum = 0.f, m_true = -INFINITY;
   int amax = 0;
   bool g_valid = false;
-  u32x4 pf[2] = {z4, z4};
+  u32x4 pf = z4;  // P^T operand of tile t-2
+  f32x4 lg[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  // partial-logit exchange positions: lane (g, r) writes at 16g + ((r + 4g) & 15)
+  const int xw = 16 * g + ((r + 4 * g) & 15);
+  const int xr = 16 * (q >> 1) + ((8 * (w & 1) + rho + 4 * (q >> 1)) & 15);
 
-  // max with the lowest id on ties, over the 8 lanes of a row (DPP: swap
-  // neighbours, swap pairs, mirror the two quads)
-  auto row_argmax = [](float& m, int& a) {
-    auto step = [&](float om, int oa) {
-      const bool take = om > m || (om == m && oa < a);
-      m = take ? om : m;
-      a = take ? oa : a;
-    };
-    step(__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)),
-         __builtin_amdgcn_update_dpp(0, a, 0xB1, 0xF, 0xF, false));
-    step(__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)),
-         __builtin_amdgcn_update_dpp(0, a, 0x4E, 0xF, 0xF, false));
-    step(__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)),
-         __builtin_amdgcn_update_dpp(0, a, 0x141, 0xF, 0xF, false));
-  };
-  auto row_sum = [](float s) {
-    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));
-    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
-    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x141, 0xF, 0xF, false));
-    return s;
-  };
-
+  for (int e = threadIdx.x; e < 2 * 2 * 32; e += 256) (&Pbuf[0][0][0])[e] = z4;
+  if (threadIdx.x < 8) (&flags[0][0])[threadIdx.x] = 0;
   int t = 0;
+  bool top_done = false;  // iteration t's barrier and reads already ran (it stopped for a fold)
+  bool fold_now = false;
   for (;;) {  // segments
-    f32x4 acc[NCH][2][2];  // [chunk][kb][h]
+    f32x16 acc[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) acc[c][k >> 1][k & 1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool fold_now = false;
-    for (;; ++t) {  // tiles
-      const bool have = t < nt;
-      f32x4 lg[2][2];  // [j][h]
-#pragma unroll
-      for (int k = 0; k < 4; ++k) lg[k >> 1][k & 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NCH; ++c) acc[c] = zero16();
+    bool last = false;
+    for (;; ++t) {  // iterations: logits(t), softmax(t-1), P.E(t-2)
+      if (!top_done) {
+        // every wave's partial logits of tile t-1 (written at the end of the
+        // previous iteration) and the softmax of tile t-2 become visible
+        __syncthreads();
+        pf = Pbuf[t & 1][h2][m32];
+        const int* fl = flags[t & 1];
+        fold_now = t >= 2 && (fl[0] | fl[1] | fl[2] | fl[3]) != 0;
+        if (fold_now) {
+          top_done = true;  // fold before P.E(t-2), then run iteration t
+          break;
+        }
+      }
+      top_done = false;
+      const bool more = t <= nt;  // an iteration t = nt + 1 only finishes P.E(nt - 1)
+      DG_LDS u16* tile = (DG_LDS u16*)&Et[t & 1][w][0][0];
+      const int tp = (t - 1) & 1;                            // parity of tile t-1
+      const bool prev_ok = t >= 1 && t - 1 < nt;             // step t-1 is a real tile
+      const int v1 = vs + 16 * (prev_ok ? phys(t - 1) : 0);  // its first id
+      float x0 = 0.f, x1 = 0.f, tm = -INFINITY;
+      int ta = 0;
+      f32x4 xa[4];
+      lg[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      lg[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int slot = c % PF;
-        // Branch-free body: on the first tile P = 0 and the LDS tile is zero;
-        // on the drain pass (t == nt) the logits are computed and discarded.
-        const u32x4 e0 = ring0[slot], e1 = ring1[slot];
-        mfma16x32_v(e0, zf[0][c], lg[0][0]);
-        mfma16x32_v(e0, zf[1][c], lg[0][1]);
-        mfma16x32_v(e1, zf[0][c], lg[1][0]);
-        mfma16x32_v(e1, zf[1][c], lg[1][1]);
-        // the transposed E of this chunk (tile t-1) was read during the
-        // previous chunk
-        acc[c][0][0] = mfma16x32(tra[0], pf[0], acc[c][0][0]);
-        acc[c][0][1] = mfma16x32(tra[0], pf[1], acc[c][0][1]);
-        acc[c][1][0] = mfma16x32(tra[1], pf[0], acc[c][1][0]);
-        acc[c][1][1] = mfma16x32(tra[1], pf[1], acc[c][1][1]);
-        // read the next chunk of tile t-1 (chunk c+1 is only overwritten in
-        // the next chunk, after this read)
-        if (c + 1 < NCH) tr_load(c + 1);
-        // 8-byte LDS writes run at twice the rate of 16-byte ones; lanes of
-        // odd g write their upper half first so that the 32 lanes of each
-        // half-wave cover all 64 banks
-        {
-          const bool odd = g & 1;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const u32x4 e = j ? e1 : e0;
-            const u32x2 lo = {e[0], e[1]}, hi = {e[2], e[3]};
-            DG_LDS u16* wp = wrb[j] + 32 * c;
-            *(DG_LDS u32x2*)(wp + (odd ? 4 : 0)) = odd ? hi : lo;
-            *(DG_LDS u32x2*)(wp + (odd ? 0 : 4)) = odd ? lo : hi;
-          }
-        }
+        const u32x4 e = ring[slot];
+        mfma16x32_v(e, zf[0][c], lg[0]);
+        mfma16x32_v(e, zf[1][c], lg[1]);
+        acc[c] = mfma32(tra[c & 1], pf, acc[c]);
+        // chunk c+2 of tile t-2 (overwritten only two chunks later, after
+        // this read), or chunks 0 and 1 of tile t-1 for the next iteration
+        if (c + 2 < NCH)
+          tr_load(tile, c + 2, c & 1);
+        else if (NCH > 1)
+          tr_load((const DG_LDS u16*)&Et[(t + 1) & 1][w][0][0], c + 2 - NCH, c & 1);
+        else
+          tr_load((const DG_LDS u16*)&Et[(t + 1) & 1][w][0][0], 0, 0);
+        // 8-byte LDS writes run at twice the rate of 16-byte ones (the tiled
+        // layout puts each lane's halves in the order that keeps them
+        // conflict-free)
+        *(DG_LDS u32x2*)(tile + wr_a + 32 * c) = u32x2{e[0], e[1]};
+        *(DG_LDS u32x2*)(tile + wr_b + 32 * c) = u32x2{e[2], e[3]};
         if (c + PF < NCH)
           issue(slot, t, c + PF);
         else
           issue(slot, t + 1, c + PF - NCH);
+
+        // ---- softmax of tile t-1, spread over the chunks ----
+        if (c == kRdX) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) xa[s] = xch[tp][s][w >> 1][xr];
+        }
+        if (c == kSum) {
+          const f32x4 a = ((xa[0] + xa[1]) + xa[2]) + xa[3];
+          const bool hi2 = q & 1;  // ids 2q, 2q+1 are elements 2(q & 1) + (0, 1)
+          const int id = v1 + 2 * q;
+          x0 = prev_ok && id < ve ? (hi2 ? a[2] : a[0]) : -INFINITY;
+          x1 = prev_ok && id + 1 < ve ? (hi2 ? a[3] : a[1]) : -INFINITY;
+          const bool second = x1 > x0;
+          tm = second ? x1 : x0;
+          ta = second ? id + 1 : id;
+          argmax_step<0xB1>(tm, ta);
+        }
+        if (c == kRed) {
+          argmax_step<0x4E>(tm, ta);
+          argmax_step<0x141>(tm, ta);
+        }
+        if (c == kExp) {
+          // tiles come out of id order: ties go to the lower id
+          const bool better = (tm > m_true) | ((tm == m_true) & (tm != -INFINITY) & (ta < amax));
+          amax = better ? ta : amax;
+          m_true = fmaxf(m_true, tm);
+          // Lazy reference: it only moves when a logit exceeds it by more than
+          // kLazyTh; the running sum is then rescaled by s = e^(m_old - m_new).
+          const bool first = m_seg == -INFINITY;
+          const bool over = !first & (tm > m_seg + kLazyTh);
+          const float s = over ? exp2f((m_seg - tm) * kLog2e) : 1.f;
+          m_seg = (first | over) ? tm : m_seg;
+          // the normaliser sums the fp32 probabilities; bf16 copies feed P.E
+          const float p0 = x0 == -INFINITY ? 0.f : exp2f((x0 - m_seg) * kLog2e);
+          const float p1 = x1 == -INFINITY ? 0.f : exp2f((x1 - m_seg) * kLog2e);
+          lsum = lsum * s + (p0 + p1);
+          *(DG_LDS uint32_t*)((DG_LDS char*)&Pbuf[tp][q >> 2][orow] + 4 * (q & 3)) = pack_bf16x2(p0, p1);
+          if (q == 0) Sbuf[tp][orow] = s;
+          const bool need_w = __any(s != 1.f);
+          if (l == 0) flags[tp][w] = need_w ? 1 : 0;
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      tr_load(0);  // chunk 0 of this tile, for the next tile's P.E
-      mfma_v_settle(lg);
-      if (!have) break;
-
-      // exchange the d-slice partials
+      mfma_v_settle(lg[0], lg[1]);
+      // this tile's partial logits, for the owners in the next iteration
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int j = k >> 1, h = k & 1;
-        xch[w][k][16 * g + ((r + 2 * g + 8 * j) & 15)] = lg[j][h];
-      }
-      __syncthreads();
-      const int v0 = vs + t * 32;
-      {
-        const int pos = 16 * og + ((orow + 2 * og + 8 * oj) & 15), blk = 2 * oj + ho;
-        f32x4 a = xch[0][blk][pos];
-        a += xch[1][blk][pos];
-        a += xch[2][blk][pos];
-        a += xch[3][blk][pos];
-        const int id0 = v0 + 16 * oj + 4 * og;
-        float x[4], tm = -INFINITY;
-        int ta = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = id0 + i < ve ? a[i] : -INFINITY;
-          const bool gt = x[i] > tm;  // ids increase with i: the first maximum is kept
-          tm = gt ? x[i] : tm;
-          ta = gt ? id0 + i : ta;
-        }
-        row_argmax(tm, ta);
-        amax = tm > m_true ? ta : amax;  // earlier tiles win ties
-        m_true = fmaxf(m_true, tm);
-        // Lazy reference: it only moves when a logit exceeds it by more than
-        // kLazyTh; the accumulated sums are then rescaled by s = e^(m_old - m_new).
-        float s = 1.f;
-        if (m_seg == -INFINITY) {
-          m_seg = tm;  // first tile of the split
-        } else if (tm > m_seg + kLazyTh) {
-          s = exp2f((m_seg - tm) * kLog2e);
-          lsum *= s;
-          m_seg = tm;
-        }
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // the normaliser sums the fp32 probabilities; bf16 copies feed P.E
-          p[i] = x[i] == -INFINITY ? 0.f : exp2f((x[i] - m_seg) * kLog2e);
-          lsum += p[i];
-        }
-        *(DG_LDS u32x2*)((DG_LDS char*)&Pbuf[ho][og][orow] + 8 * oj) =
-            u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-        if ((l & 7) == 0) Sbuf[16 * ho + orow] = s;
-        const bool need = __any(s != 1.f);
-        if (l == 0) flags[w] = need ? 1 : 0;
-      }
-      __syncthreads();
-      pf[0] = Pbuf[0][g][r];
-      pf[1] = Pbuf[1][g][r];
-      if (flags[0] | flags[1] | flags[2] | flags[3]) {
-        fold_now = true;  // fold before this tile's P.E
+      for (int h = 0; h < 2; ++h) xch[t & 1][w][h][xw] = lg[h];
+      if (!more) {
+        last = true;
         break;
       }
     }
 
     // Fold the segment into G with the per-row factor s: G = (G + acc) s
-    // (G = acc s on the first fold; s = 1 at the end of the split).  The
-    // accumulator is only ever stored raw (never touched by VALU code, so it
-    // stays in AGPRs): the first fold stores it to G, a later one to the temp
-    // area T, which is then merged with plain loads and stores.
-    float s2[2] = {1.f, 1.f};
-    if (fold_now) {
-      s2[0] = Sbuf[r];
-      s2[1] = Sbuf[16 + r];
-    }
-    const bool merge = g_valid || fold_now;
+    // (G = acc s on the first fold; s = 1 at the end of the split).  The first
+    // fold stores the raw accumulator to G, a later one to the temp area T,
+    // which is then merged with plain loads and stores.
+    const int zr = r0 + m32;
+    const float s = fold_now ? Sbuf[t & 1][m32] : 1.f;
+    if (zr < R) {
+      float* gp = pS + ((size_t)split * R + zr) * d + dbase + 4 * h2;
+      float* dst = g_valid ? gp + tofs : gp;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int zr = r0 + 16 * h + r;
-      if (zr < R) {
-        float* gp = pS + ((size_t)split * R + zr) * d + dbase + 4 * g;
-        float* dst = g_valid ? gp + tofs : gp;
+      for (int c = 0; c < NCH; ++c)
 #pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *(f32x4*)(dst + 32 * c + 8 * j) =
+              f32x4{acc[c][4 * j], acc[c][4 * j + 1], acc[c][4 * j + 2], acc[c][4 * j + 3]};
+      if (g_valid || fold_now) {
         for (int c = 0; c < NCH; ++c)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) *(f32x4*)(dst + 32 * c + 16 * kb) = acc[c][kb][h];
-        if (merge) {
-          for (int c = 0; c < 2 * NCH; ++c) {
-            float* q = gp + 16 * c;
-            f32x4 v = *(const f32x4*)q;
-            if (g_valid) v += *(const f32x4*)(q + tofs);
-            *(f32x4*)q = v * s2[h];
+          for (int j = 0; j < 4; ++j) {
+            float* p = gp + 32 * c + 8 * j;
+            f32x4 v = *(const f32x4*)p;
+            if (g_valid) v += *(const f32x4*)(p + tofs);
+            *(f32x4*)p = v * s;
           }
-        }
       }
     }
     g_valid = true;
-    if (!fold_now) break;
-    ++t;
+    if (last) break;
+    fold_now = false;
   }
 
-  const float tot = row_sum(lsum);
-  const int zr = r0 + 16 * ho + orow;
-  if (zr < R && (l & 7) == 0)
-    pstat[(size_t)split * R + zr] = f32x4{m_seg, tot, m_true, __int_as_float(amax)};
+  const float tot = sum8(lsum);
+  if (r0 + orow < R && q == 0)
+    pstat[(size_t)split * R + r0 + orow] = f32x4{m_seg, tot, m_true, __int_as_float(amax)};
 }
 
 // ---------------------------------------------------------------------------
@@ -410,7 +429,7 @@ __global__ void __launch_bounds__(256, 1)
   {
     const u16* zp = Z + (size_t)(zok ? zr : R - 1) * d + dbase + g4 * 8;
 #pragma unroll
-    for (int ks = 0; ks < NCH; ++ks) zf[ks] = ldg128(zp + ks * 32);
+    for (int ks = 0; ks < NCH; ++ks) zf[ks] = swap_halves(ldg128(zp + ks * 32), g4 & 1);
   }
   float* gp = pS + ((size_t)split * R + (zok ? zr : 0)) * d + dbase + 4 * g4;
   const size_t tofs = (size_t)gridDim.x / nrb * R * d;
@@ -477,7 +496,8 @@ __global__ void __launch_bounds__(256, 1)
           const u32x2 a = lds_read_tr16(trb + c * 32 + 16 * p);
           acc[2 * c + p] = mfma16x16(a, pf, acc[2 * c + p]);
         }
-        *(DG_LDS u32x4*)(wrb + c * 32) = e0;
+        *(DG_LDS u32x2*)(wrb + c * 32 + ((g4 & 1) ? 4 : 0)) = u32x2{e0[0], e0[1]};
+        *(DG_LDS u32x2*)(wrb + c * 32 + ((g4 & 1) ? 0 : 4)) = u32x2{e0[2], e0[3]};
         if (c + PF < NCH)
           issue(slot, t, c + PF);
         else
@@ -690,8 +710,9 @@ __global__ void __launch_bounds__(256) k_vocab_f32(int R, int d, int V, const fl
 
 // ---------------------------------------------------------------------------
 // Tiled table: thread q writes 16 bytes of block q / 64 at lane position
-// q % 64 = 16 g + r: id 16 vb + r, columns 32 c + 8 g .. +7, where the block
-// is (vb, c) = (q / 64 / (d/32), q / 64 % (d/32)); ids past V are zero.
+// q % 64 = 16 g + r: id 16 vb + r, columns 32 c + 8 g .. +7 (for odd g the
+// two 8-byte halves swapped), where the block is (vb, c) =
+// (q / 64 / (d/32), q / 64 % (d/32)); ids past V are zero.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) k_pack_embedding(int V, int d, size_t n16, const u16* __restrict__ E,
                                                         u32x4* __restrict__ out) {
@@ -702,7 +723,7 @@ __global__ void __launch_bounds__(256) k_pack_embedding(int V, int d, size_t n16
   const size_t cpb = (size_t)d / 32;
   const size_t vb = b / cpb, c = b % cpb;
   const size_t id = vb * 16 + r;
-  out[q] = id < (size_t)V ? ldg128(E + id * d + c * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+  out[q] = id < (size_t)V ? swap_halves(ldg128(E + id * d + c * 32 + g * 8), g & 1) : u32x4{0u, 0u, 0u, 0u};
 }
 
 hipError_t launch_pack_embedding(int V, int d, const void* E, void* E_tiled, hipStream_t s) {
@@ -722,7 +743,7 @@ VocabPlan vocab_plan(int rows, int d, int V, int dtype) {
     return p;
   }
   int rw, vt;
-  if (d <= 2048) { p.variant = 1; rw = 32; vt = 32; }
+  if (d <= 2048) { p.variant = 1; rw = 32; vt = 16; }
   else { p.variant = 2; rw = 16; vt = 16; }
   p.nrb = (rows + rw - 1) / rw;
   const int tiles = (V + vt - 1) / vt;
