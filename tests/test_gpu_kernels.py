@@ -105,6 +105,9 @@ def test_tiled_embedding_layout(V, d):
     (40, 256, 1000, "bf16"),                              # 32-row tiles: ragged rows and ids
     (70, 128, 4133, "bf16"),
     (256, 2048, 32768, "bf16"),                           # the 32k-vocab step's shape, every row
+    (100, 2048, 5000, "bf16"),                            # CU pairs: ragged 64-row block
+    (1, 2048, 200, "bf16"),                               # splits of 2, 1 and 0 tiles
+    (130, 2048, 7001, "bf16"),                            # 3 row blocks x 40 splits, ragged ids
     (37, 4096, 3000, "bf16"),                             # 16-row tiles (d = 4096)
 ])
 def test_vocab_matches_oracle(R, d, V, dtype):
@@ -119,16 +122,19 @@ def test_vocab_matches_oracle(R, d, V, dtype):
     close("c", c, rc, tol)
     close("S", S, rS, tol, rel)
     argmax_match("argmax", a, ra, top2_gap(Zf, Ef), rm)
-    assert 0.1 < rc.mean() < 0.95   # the inputs exercise a non-trivial softmax
+    if R >= 16:
+        assert 0.1 < rc.mean() < 0.95   # the inputs exercise a non-trivial softmax
 
 
-@pytest.mark.parametrize("d,V,rows", [(2048, 262144, 256), (4096, 262144, 256)])
+@pytest.mark.parametrize("d,V,rows", [(2048, 262144, 256), (4096, 262144, 256), (2048, 262144, 2048)])
 def test_vocab_full_vocab_sampled_rows(d, V, rows):
     say(f"vocab full-size d={d} V={V} R={rows} (sampled rows)")
-    E, Z = _vocab_inputs(rows, d, V, "bf16", seed=d)
+    E, Z = _vocab_inputs(rows, d, V, "bf16", seed=d + rows)
     m, a, c, lse, S = _run_vocab(rows, d, V, E, Z, "bf16")
     Ef, Zf = as_f64(E, "bf16"), as_f64(Z, "bf16")
-    idx = np.array([0, 1, 31, 32, 100, 127, 128, 200, 254, 255])
+    idx = np.array([0, 1, 31, 32, 63, 64, 100, 127, 128, 200, 254, 255])
+    if rows > 256:
+        idx = np.concatenate([idx, [rows // 2 - 1, rows // 2, rows - 65, rows - 64, rows - 2, rows - 1]])
     rm, ra, rlse, rc, rS, gap = step.vocab_rows(Zf[idx], Ef)
     close("m", m[idx], rm, ATOL["bf16"])
     close("lse", lse[idx], rlse, ATOL["bf16"])

@@ -70,7 +70,7 @@ int check_vocab_shape(int rows, int d, int V, int dtype) {
 
 size_t vocab_ws(int rows, int d, int V, int dtype) {
   dg::VocabPlan p = dg::vocab_plan(rows, d, V, dtype);
-  return round_up(p.part_S_bytes) + round_up(p.part_stat_bytes);
+  return round_up(p.part_S_bytes) + round_up(p.part_stat_bytes) + round_up(p.part_X_bytes);
 }
 
 size_t attn_ws(const dg_dims* d, int causal) {

@@ -64,8 +64,9 @@ __device__ __forceinline__ u32x4 ldg128(const u16* p) { return *(const u32x4*)p;
 // the hipError_t of its launch.  Pointers and sizes are already validated.
 namespace dg {
 struct VocabPlan {
-  int rows, d, V, nrb, nsplit, split_len, variant;  // variant: 0 fp32 rowwise, 1 bf16 32-row, 2 bf16 16-row
-  size_t part_S_bytes, part_stat_bytes;
+  // variant: 0 fp32 rowwise, 1 bf16 32-row, 2 bf16 16-row, 3 bf16 64-row CU pairs
+  int rows, d, V, nrb, nsplit, split_len, variant;
+  size_t part_S_bytes, part_stat_bytes, part_X_bytes;  // X: pair exchange (variant 3)
 };
 VocabPlan vocab_plan(int rows, int d, int V, int dtype);
 // ev_begin / ev_end (may be NULL) are recorded around the main kernel only.

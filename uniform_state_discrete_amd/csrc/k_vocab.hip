@@ -51,6 +51,9 @@ __device__ __forceinline__ void mfma16x32_v(u32x4 a, u32x4 b, f32x4& d) {
 __device__ __forceinline__ void mfma_v_settle(f32x4 (&lg)[2][2]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(lg[0][0]), "+v"(lg[0][1]), "+v"(lg[1][0]), "+v"(lg[1][1]));
 }
+__device__ __forceinline__ void mfma_v_settle(f32x4 (&lg)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(lg[0]), "+v"(lg[1]), "+v"(lg[2]), "+v"(lg[3]));
+}
 __device__ __forceinline__ void mfma_v_settle(f32x4& a, f32x4& b) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
 }
@@ -574,20 +577,463 @@ __global__ void __launch_bounds__(256, 1)
 }
 
 // ---------------------------------------------------------------------------
+// Variant 64p (d = 8*SLICE): two workgroups on one XCD share 64 rows.  With
+// 32 rows per workgroup every E byte feeds too little matrix-core work: one
+// 64-cycle chunk needs 4 KiB of E from L2 and 8 KiB of LDS traffic per CU,
+// more than either path delivers.  Here a workgroup owns 64 rows and one half
+// of the columns of S = P.E (so its accumulators still fit the AGPR file):
+// per 16-id tile it reads only its half of E (32 KiB) for 2x the rows.  The
+// logits need the full-width contraction, so the two halves swap their
+// partial logits through the XCD's L2: each writes its 64 x 16 partial as
+// 64-bit words {value, tile tag} and polls the other's until all tags match
+// (no ordering between stores is needed; both sum in the same order, so both
+// compute bit-identical softmax results).  Every poll loop is bounded: on
+// timeout it raises an error flag (the combine then writes NaN) and stops
+// waiting, so no wave can hang.
+//
+// Pairing: workgroup = 4 waves, one per SIMD, one per CU (LDS).  A workgroup
+// reads its XCD id from the hardware and takes a ticket from that XCD's
+// counter; tickets 2k and 2k+1 on XCD x form pair x * (grid/16) + k (half =
+// ticket & 1), so partners always share an L2 whatever the dispatch order.
+// The counters and tags are cleared by k_vocab_pair_clear before each launch.
+//
+// Pipeline (iteration t, 8 chunks of 32 columns per wave):
+//   logits of tile t            all chunks (E streamed through registers)
+//   partial of tile t-1         LDS exchange of the 4 waves, summed, stored
+//   softmax of tile t-2         after the other half's partial arrived
+//   P.E of tile t-3             from the 4-deep LDS ring of E tiles
+// Barriers sit at chunk boundaries where the LDS operations before them were
+// issued a full chunk of matrix-core work earlier.
+// ---------------------------------------------------------------------------
+constexpr int kPairSlots = 4;                // exchange ring depth, in tiles
+constexpr uint32_t kPairSpin = 1u << 20;     // poll bound of one exchange
+// header words: 0-7 tickets per XCD, 8 error flag, 9 exchange waits that
+// had to poll, 10 poll timeouts, 11 workgroups without a ticket, 12-15 the
+// first timeout (pair, iteration, half | wave << 4, lane 0's generation bit)
+constexpr int kPairHdrWords = 64;            // 256 bytes
+constexpr size_t kPairRecBytes = 2 * kPairSlots * 256 * 16;  // per pair
+
+// Exchange record of a lane: its 4 partial logits, each fp32 carrying the
+// slot generation (tile / 4) & 1 in its lowest mantissa bit.  A slot is
+// reused every 4 tiles and a reader is never more than one generation
+// behind, so one bit tells the wanted tile from the one before it; each
+// 4-byte word is single-copy atomic, so a reader accepts the record once all
+// four bits match.  The bit moves a partial by at most one ulp, and both
+// halves add the same tagged values in the same order.  The partners share
+// an XCD: the store (through a buffer resource: no 64-bit lane address)
+// reaches that XCD's L2, the vector L1 being write-through; the load is a
+// device-scope global load, which misses the L1.  (A device-scope buffer
+// load kept returning the L1's stale line on gfx950, in a ping-pong probe
+// between paired workgroups.)
+__device__ __forceinline__ f32x4 pair_tagged(f32x4 v, uint32_t gen) {
+  f32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = __uint_as_float((__float_as_uint(v[i]) & ~1u) | gen);
+  return o;
+}
+__device__ __forceinline__ bool pair_gen_ok(u32x4 w, uint32_t gen) {
+  return ((w[0] & w[1] & w[2] & w[3] & 1u) == gen) & (((w[0] | w[1] | w[2] | w[3]) & 1u) == gen);
+}
+__device__ __forceinline__ u32x4 pair_load(const char* base, uint32_t off) {
+  uint64_t* p = (uint64_t*)(const_cast<char*>(base) + off);
+  const uint64_t a = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
+
+template <int SLICE>
+__global__ void __launch_bounds__(256, 1)
+    k_vocab_pair(const u16* __restrict__ Z, const u16* __restrict__ E, int R, int d, int V, int nrb,
+                 int split_len, float* __restrict__ pS, f32x4* __restrict__ pstat,
+                 uint32_t* __restrict__ xhdr, uint64_t* __restrict__ xrec) {
+  constexpr int NCH = SLICE / 32, EP = SLICE + 8;
+  static_assert(NCH == 8, "the stage schedule assumes 8 chunks per tile");
+  __shared__ __attribute__((aligned(16))) u16 Et[4][4][16][EP];     // [tile & 3][wave]
+  __shared__ __attribute__((aligned(16))) f32x4 xch[4][4][64];      // [writer wave][row group][rotated lane]
+  __shared__ __attribute__((aligned(16))) u32x4 Pbuf[2][64];        // P of row m, ids 8k..8k+7
+  __shared__ float Sbuf[64];                                        // per-row fold factor
+  __shared__ __attribute__((aligned(16))) int flags[4];
+  __shared__ __attribute__((aligned(16))) f32x4 ownb[256];          // this half's partial, owner lane
+  __shared__ int role[2];
+
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, r = l & 15;
+  const int h2 = l >> 5, m32 = l & 31;
+  if (threadIdx.x == 0) {
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xFu;  // HW_REG_XCC_ID
+    const uint32_t quota = gridDim.x / 8;
+    int pr = -1, half = 0;
+    if (xcc < 8) {
+      const uint32_t tk = __hip_atomic_fetch_add(&xhdr[xcc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tk < quota) {
+        pr = (int)(xcc * (quota / 2) + tk / 2);
+        half = (int)(tk & 1);
+      }
+    }
+    if (pr < 0) {
+      __hip_atomic_store(&xhdr[8], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&xhdr[11], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    role[0] = pr;
+    role[1] = half;
+  }
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  for (int e = threadIdx.x; e < 2 * 64; e += 256) (&Pbuf[0][0])[e] = z4;
+  if (threadIdx.x < 4) flags[threadIdx.x] = 0;
+  {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      DG_LDS u16* ep = (DG_LDS u16*)&Et[b][w][0][0];
+      for (int e = l * 8; e < 16 * EP; e += 64 * 8) *(DG_LDS u32x4*)(ep + e) = z4;
+    }
+  }
+  __syncthreads();
+  const int pair = __builtin_amdgcn_readfirstlane(role[0]), hf = __builtin_amdgcn_readfirstlane(role[1]);
+  if (pair < 0) return;  // the whole workgroup: no ticket (error raised)
+  const int rb = pair % nrb, split = pair / nrb;
+  const int r0 = rb * 64;
+  const int vs = split * split_len, ve = min(V, vs + split_len);
+  const int dbase = hf * (d >> 1) + w * SLICE;
+  const size_t tofs = (size_t)gridDim.x / 2 / nrb * R * d;  // temp area follows the nsplit partials
+
+  // Z fragments of rows 16h + r, columns dbase + 32c + 8g .. +7
+  u32x4 zf[4][NCH];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const u16* zp = Z + (size_t)min(r0 + 16 * h + r, R - 1) * d + dbase + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) zf[h][c] = swap_halves(ldg128(zp + 32 * c), g & 1);
+  }
+
+  const int nt = ve > vs ? (ve - vs + 15) / 16 : 0;
+  // the 4 row blocks that stream one split start at different tiles of each
+  // round of 4, so one step fetches 4 distinct tiles from HBM
+  const int nt4 = nt & ~3;
+  auto phys = [&](int s) { return s < nt4 ? (s & ~3) | ((s + rb) & 3) : s; };
+
+  const int wr_a = prow16t(r) * EP + 8 * g + ((g & 1) ? 4 : 0), wr_b = wr_a ^ 4;
+  int tr_off[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    tr_off[k] = prow16t(8 * h2 + 4 * k + ((l & 15) >> 2)) * EP + 16 * ((l >> 4) & 1) + 4 * (l & 3);
+
+  const uint32_t blk_row = (uint32_t)d * 32u;
+  const __amdgpu_buffer_rsrc_t erc = buffer_rsrc(E, (uint32_t)(((size_t)V + 15) / 16 * blk_row));
+  const uint32_t lane_off = (uint32_t)((size_t)(vs / 16) * blk_row + (size_t)(dbase / 32) * 1024u + l * 16u);
+  u32x4 ring[NCH];
+  auto issue = [&](int c, int step) {
+    ring[c] = buffer_ld128(erc, lane_off + (uint32_t)phys(step) * blk_row + 1024u * c);
+  };
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) issue(c, 0);
+
+  u32x4 tra[2];
+  auto tr_load = [&](const DG_LDS u16* tile, int c, int slot) {
+    const u32x2 a = lds_read_tr16(tile + tr_off[0] + 32 * c);
+    const u32x2 b = lds_read_tr16(tile + tr_off[1] + 32 * c);
+    tra[slot] = u32x4{a[0], a[1], b[0], b[1]};
+  };
+  tr_load((const DG_LDS u16*)&Et[1][w][0][0], 0, 0);  // tile -3: zeros
+  tr_load((const DG_LDS u16*)&Et[1][w][0][0], 1, 1);
+
+  // softmax owner: row 16w + rho, ids 4q .. 4q+3 (lane 4 rho + q)
+  const int rho = l >> 2, q = l & 3, orow = 16 * w + rho;
+  float m_seg = -INFINITY, lsum = 0.f, m_true = -INFINITY;
+  int amax = 0;
+  bool g_valid = false, broken = false;
+  u32x4 pf[2] = {z4, z4};
+  f32x4 lg[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) lg[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 own_old = {0.f, 0.f, 0.f, 0.f};
+  u32x4 xp = z4;
+  const int xw = 16 * g + ((r + 4 * g) & 15);
+  const int xr = 16 * q + ((rho + 4 * q) & 15);
+  // exchange records: [pair][half][slot][256 lanes][4 words]; uniform bases
+  // plus a 32-bit lane offset
+  const __amdgpu_buffer_rsrc_t xrc = buffer_rsrc(xrec, (uint32_t)(gridDim.x / 2 * kPairRecBytes));
+  const uint32_t xo_out = (uint32_t)((pair * 2 + hf) * kPairSlots) * 4096u;
+  const char* const xo_in = (const char*)xrec + (size_t)((pair * 2 + (hf ^ 1)) * kPairSlots) * 4096;
+  const uint32_t xlane = threadIdx.x * 16u;
+
+  f32x16 acc[2][NCH];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) acc[hh][c] = zero16();
+
+  // G = (G + acc) s (G = acc s on the first fold; the first fold stores the
+  // raw accumulator to G, a later one to the temp area T, merged after)
+  auto fold = [&](float s, bool scale) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int zr = r0 + 32 * hh + m32;
+      if (zr < R) {
+        float* gp = pS + ((size_t)split * R + zr) * d + dbase + 4 * h2;
+        float* dst = g_valid ? gp + tofs : gp;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *(f32x4*)(dst + 32 * c + 8 * j) =
+                f32x4{acc[hh][c][4 * j], acc[hh][c][4 * j + 1], acc[hh][c][4 * j + 2], acc[hh][c][4 * j + 3]};
+      }
+    }
+    if (g_valid || scale) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int zr = r0 + 32 * hh + m32;
+        const float sr = scale ? Sbuf[32 * hh + m32] : 1.f;
+        if (zr < R) {
+          float* gp = pS + ((size_t)split * R + zr) * d + dbase + 4 * h2;
+          for (int c = 0; c < NCH; ++c)
+            for (int j = 0; j < 4; ++j) {
+              float* p = gp + 32 * c + 8 * j;
+              f32x4 v = *(const f32x4*)p;
+              if (g_valid) v += *(const f32x4*)(p + tofs);
+              *(f32x4*)p = v * sr;
+            }
+        }
+      }
+    }
+    g_valid = true;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) acc[hh][c] = zero16();
+  };
+
+  for (int t = 0; t <= nt + 2; ++t) {
+    // Tile t-1's partial logits and tile t-3's softmax output (written in
+    // the previous iteration) become visible.
+    __syncthreads();
+    pf[0] = Pbuf[h2][m32];
+    pf[1] = Pbuf[h2][32 + m32];
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    i32x4_t flv = *(const DG_LDS i32x4_t*)flags;  // combined after chunk 0's logit products
+    const bool own_ok = t >= 1 && t - 1 < nt;  // tile t-1 is exchanged
+    const bool sm_ok = t >= 2 && t - 2 < nt;   // tile t-2 gets its softmax
+    const int v2 = vs + 16 * (sm_ok ? phys(t - 2) : 0);
+    DG_LDS u16* tile = (DG_LDS u16*)&Et[t & 3][w][0][0];
+    const DG_LDS u16* tpe = (const DG_LDS u16*)&Et[(t + 1) & 3][w][0][0];   // tile t-3
+    const DG_LDS u16* tnx = (const DG_LDS u16*)&Et[(t + 2) & 3][w][0][0];   // tile t-2
+    f32x4 xa[4], own;
+    float x[4];
+    float tm = -INFINITY, s = 1.f, ms = 0.f;
+    bool over = false, first = false;
+    // The softmax of tile t-2 and the exchange of tile t-1, cut into small
+    // steps: step (c, j) runs right after matrix-core instruction j of chunk
+    // c (j = 0..3 logits, 4..5 self-conditioning), so the latency of its
+    // dependent vector instructions overlaps the product in flight instead
+    // of idling the matrix core.
+    auto stage = [&](int c, int j) {
+      if (c == 2 && j == 0) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) xa[s4] = xch[s4][w][xr];
+      }
+      if (c == 3 && j == 0) {
+        own_old = ownb[threadIdx.x];  // this half's partial of tile t-2, parked last iteration
+        own = xa[0] + xa[1];
+      }
+      if (c == 3 && j == 1) own = (own + xa[2]) + xa[3];
+      if (c == 3 && j == 2) {
+        own = pair_tagged(own, (uint32_t)((t - 1) >> 2) & 1u);
+        ownb[threadIdx.x] = own;
+      }
+      if (c == 3 && j == 3 && own_ok)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, own), xrc, xlane,
+                                               xo_out + ((t - 1) & 3) * 4096u, 0);
+      if (c == 4 && j == 0 && sm_ok) {
+        const uint32_t want = (uint32_t)((t - 2) >> 2) & 1u;  // generation of tile t-2
+        bool ok = pair_gen_ok(xp, want);
+        if (!__all(ok) && !broken) {
+          if (l == 0) __hip_atomic_fetch_add(&xhdr[9], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const char* so = xo_in + ((t - 2) & 3) * 4096;
+          for (uint32_t n = 0;; ++n) {
+            xp = pair_load(so, xlane);
+            ok = pair_gen_ok(xp, want);
+            if (__all(ok)) break;
+            if (n >= kPairSpin) {
+              broken = true;
+              if (l == 0) {
+                __hip_atomic_store(&xhdr[8], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (__hip_atomic_fetch_add(&xhdr[10], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+                  xhdr[12] = (uint32_t)pair;
+                  xhdr[13] = (uint32_t)t;
+                  xhdr[14] = (uint32_t)(hf | (w << 4));
+                  xhdr[15] = xp[0] & 1u;
+                }
+              }
+              break;
+            }
+          }
+        }
+      }
+      if (c == 4 && j == 1) {
+        // both halves add half 0's partial first
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __uint_as_float(xp[i]);
+          x[i] = hf == 0 ? own_old[i] + pv : pv + own_old[i];
+        }
+      }
+      if (c == 4 && j == 2 && !(sm_ok && v2 + 16 <= ve)) {
+        // a ragged or absent tile (uniform): ids past the split are -inf
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = sm_ok && v2 + 4 * q + i < ve ? x[i] : -INFINITY;
+      }
+      if (c == 4 && j == 3) tm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (c == 4 && j == 4) tm = fmaxf(tm, dpp_f<0xB1>(tm));
+      if (c == 4 && j == 5) tm = fmaxf(tm, dpp_f<0x4E>(tm));  // the row's tile max, in all 4 lanes
+      if (c == 5 && j == 0 && __any(tm >= m_true)) {
+        // the running max may move (uniform branch, rare after a split's
+        // first tiles): lowest id attaining the tile max; tiles come out of
+        // id order, so a tie goes to the lower id
+        int cand = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) cand = x[i] == tm ? v2 + 4 * q + i : cand;
+        cand = min(cand, dpp_i<0xB1>(cand));
+        cand = min(cand, dpp_i<0x4E>(cand));
+        const bool better = (tm > m_true) | ((tm == m_true) & (tm != -INFINITY) & (cand < amax));
+        amax = better ? cand : amax;
+        m_true = fmaxf(m_true, tm);
+      }
+      if (c == 5 && j == 1) {
+        // Lazy reference: it only moves when a logit exceeds it by more than
+        // kLazyTh; the running sum is then rescaled by s = e^(m_old - m_new).
+        first = m_seg == -INFINITY;
+        over = !first & (tm > m_seg + kLazyTh);
+        s = over ? __builtin_amdgcn_exp2f((m_seg - tm) * kLog2e) : 1.f;
+      }
+      if (c == 5 && j == 2) {
+        m_seg = (first | over) ? tm : m_seg;
+        ms = m_seg == -INFINITY ? 0.f : m_seg;  // a row with no valid logit yet: all p are 0
+      }
+      // p = 2^((x - m) log2 e): exact 1 at the maximum, 0 for a masked -inf;
+      // results below 2^-126 flush to 0 (more than 87 below the reference)
+      if (c == 5 && j == 3) {
+        x[0] = __builtin_amdgcn_exp2f((x[0] - ms) * kLog2e);
+        x[1] = __builtin_amdgcn_exp2f((x[1] - ms) * kLog2e);
+      }
+      if (c == 5 && j == 4) {
+        x[2] = __builtin_amdgcn_exp2f((x[2] - ms) * kLog2e);
+        x[3] = __builtin_amdgcn_exp2f((x[3] - ms) * kLog2e);
+      }
+      if (c == 5 && j == 5) lsum = fmaf(lsum, s, (x[0] + x[1]) + (x[2] + x[3]));
+      if (c == 6 && j == 0) {
+        typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+        typedef float f32x2v __attribute__((ext_vector_type(2)));
+        const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x[0], x[1]}, bf16x2v));
+        const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x[2], x[3]}, bf16x2v));
+        *(DG_LDS u32x2*)((DG_LDS char*)&Pbuf[q >> 1][orow] + 8 * (q & 1)) = u32x2{lo, hi};
+      }
+      if (c == 6 && j == 1) {
+        // every lane of a row writes the same factor, every lane of the wave
+        // the same flag (no branch; orow = threadIdx.x / 4)
+        Sbuf[threadIdx.x >> 2] = s;
+        flags[__builtin_amdgcn_readfirstlane(w)] = __any(s != 1.f) ? 1 : 0;
+      }
+    };
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const u32x4 e = ring[c];
+      if (c == 0) {
+        // tile t-1's partial logits of this wave (finished last iteration)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) xch[w][h][xw] = lg[h];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) lg[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      *(DG_LDS u32x2*)(tile + wr_a + 32 * c) = u32x2{e[0], e[1]};
+      *(DG_LDS u32x2*)(tile + wr_b + 32 * c) = u32x2{e[2], e[3]};
+      if (c == 7 && own_ok) {
+        // the other half's partial of tile t-1 (stored at chunk 3 of this
+        // iteration), consumed at chunk 4 of the next
+        xp = pair_load(xo_in + ((t - 1) & 3) * 4096, xlane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        mfma16x32_v(e, zf[h][c], lg[h]);
+        stage(c, h);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c == 0) {
+        // the flags' LDS latency hides behind the products above: their
+        // first use is pinned after them
+        asm volatile("" : "+v"(flv));
+        if (t >= 3 && (flv[0] | flv[1] | flv[2] | flv[3]) != 0) {
+          // tile t-3's softmax moved a reference: fold the products of the
+          // tiles before it under the old one
+          fold(0.f, true);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        acc[hh][c] = mfma32(tra[c & 1], pf[hh], acc[hh][c]);
+        stage(c, 4 + hh);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c == NCH - 1) mfma_v_settle(lg);
+      if (c == 1) __syncthreads();  // tile t-1's partials are in LDS; tile t-3's P is read
+      // A operand of chunk c+2 of tile t-3 (slot c & 1 was just consumed), or
+      // of chunks 0, 1 of tile t-2 for the next iteration
+      if (c + 2 < NCH)
+        tr_load(tpe, c + 2, c & 1);
+      else
+        tr_load(tnx, c + 2 - NCH, c & 1);
+      // chunk c of tile t+1 into the slot this chunk's products just read
+      issue(c, t + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  fold(1.f, false);
+
+  const float tot = lsum + dpp_f<0xB1>(lsum);
+  const float tot4 = tot + dpp_f<0x4E>(tot);
+  if (hf == 0 && r0 + orow < R && q == 0)
+    pstat[(size_t)split * R + r0 + orow] = f32x4{m_seg, tot4, m_true, __int_as_float(amax)};
+}
+
+// Zeroes the pair tickets, error flag and exchange tags (a kernel, so that
+// the launch sequence can be captured in a graph).
+__global__ void __launch_bounds__(256) k_vocab_pair_clear(u32x4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// ---------------------------------------------------------------------------
 // Combine of the vocab splits, one workgroup per row, splits in increasing
 // vocab order:  max = max_s max_s,  argmax = that of the first split
 // attaining it (lowest id),  mu = max_s m_ref_s,  Lt = sum_s e^(m_ref_s - mu) sum_s,
 // lse = mu + ln Lt,  conf = e^(max - mu) / Lt,  S = sum_s e^(m_ref_s - mu) S_s / Lt.
+// err (may be NULL): the paired kernel's error flag; when set, the outputs are
+// NaN (argmax -1) instead of a silently wrong result.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) k_vocab_combine(int R, int d, int nsplit, const float* __restrict__ pS,
                                                        const f32x4* __restrict__ pstat,
                                                        float* __restrict__ max_logit,
                                                        int32_t* __restrict__ argmax,
                                                        float* __restrict__ conf, float* __restrict__ lse,
-                                                       void* __restrict__ S, int out_bf16) {
+                                                       void* __restrict__ S, int out_bf16,
+                                                       const uint32_t* __restrict__ err) {
   __shared__ float wgt[1024];
   __shared__ float sh[4];
   const int r = blockIdx.x;
+  if (err && *err) {
+    // a paired split lost its partner: every output of the row is NaN
+    if (threadIdx.x == 0) {
+      max_logit[r] = NAN;
+      argmax[r] = -1;
+      conf[r] = NAN;
+      if (lse) lse[r] = NAN;
+    }
+    for (int e = threadIdx.x; e < d; e += 256) {
+      if (out_bf16) ((u16*)S)[(size_t)r * d + e] = 0x7FC0;
+      else ((float*)S)[(size_t)r * d + e] = NAN;
+    }
+    return;
+  }
   if (threadIdx.x == 0) {
     float M = -INFINITY, mu = -INFINITY;
     int A = 0;
@@ -735,6 +1181,20 @@ hipError_t launch_pack_embedding(int V, int d, const void* E, void* E_tiled, hip
 }
 
 // ---------------------------------------------------------------------------
+// CU pairs need all 8 XCDs of a full MI355X (256 CUs, one workgroup each).
+static bool pair_capable() {
+  static int cached[64];
+  static bool init[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (!init[dev]) {
+    int n = 0;
+    cached[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n == 256;
+    init[dev] = true;
+  }
+  return cached[dev] != 0;
+}
+
 VocabPlan vocab_plan(int rows, int d, int V, int dtype) {
   VocabPlan p{};
   p.rows = rows; p.d = d; p.V = V;
@@ -742,11 +1202,32 @@ VocabPlan vocab_plan(int rows, int d, int V, int dtype) {
     p.variant = 0; p.nrb = rows; p.nsplit = 1; p.split_len = V;
     return p;
   }
-  int rw, vt;
-  if (d <= 2048) { p.variant = 1; rw = 32; vt = 16; }
-  else { p.variant = 2; rw = 16; vt = 16; }
+  const int vt = 16, tiles = (V + vt - 1) / vt;
+  if (d == 2048 && (rows + 63) / 64 <= 128 && pair_capable()) {
+    // CU pairs, 64 rows: 2 nrb nsplit = 256 workgroups at most, a multiple
+    // of 16 so that every XCD holds whole pairs
+    const int nrb = (rows + 63) / 64;
+    int ns = 128 / nrb;
+    while (ns > 0 && (nrb * ns) % 8 != 0) --ns;
+    if (ns > tiles) {
+      ns = tiles;
+      while (ns > 0 && (nrb * ns) % 8 != 0) --ns;
+    }
+    if (ns > 0) {
+      p.variant = 3;
+      p.nrb = nrb;
+      p.split_len = (tiles + ns - 1) / ns * vt;
+      p.nsplit = ns;  // trailing splits may be empty: they contribute nothing
+      p.part_S_bytes = 2 * (size_t)p.nsplit * rows * d * sizeof(float);
+      p.part_stat_bytes = (size_t)p.nsplit * rows * sizeof(f32x4);
+      p.part_X_bytes = 256 + kPairHdrWords * 4 + (size_t)nrb * ns * kPairRecBytes;
+      return p;
+    }
+  }
+  int rw;
+  if (d <= 2048) { p.variant = 1; rw = 32; }
+  else { p.variant = 2; rw = 16; }
   p.nrb = (rows + rw - 1) / rw;
-  const int tiles = (V + vt - 1) / vt;
   int ns = (256 + p.nrb / 2) / p.nrb;              // one workgroup per CU
   ns = ns < 1 ? 1 : (ns > tiles ? tiles : ns);
   p.split_len = (tiles + ns - 1) / ns * vt;
@@ -775,11 +1256,22 @@ hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float*
   const u16* Eb = (const u16*)E;
   const int sl = p.d / 4;
   bool launched = true;
+  uint32_t* xhdr = nullptr;
+  if (p.variant == 3) {
+    xhdr = (uint32_t*)(((uintptr_t)ws + p.part_S_bytes + p.part_stat_bytes + 255) & ~(uintptr_t)255);
+    const size_t xbytes = kPairHdrWords * 4 + (size_t)p.nrb * p.nsplit * kPairRecBytes;
+    hipLaunchKernelGGL(k_vocab_pair_clear, dim3(512), dim3(256), 0, s, (u32x4*)xhdr, xbytes / 16);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
   if (ev_begin) {
     hipError_t e = hipEventRecord(ev_begin, s);
     if (e != hipSuccess) return e;
   }
-  if (p.variant == 1) {
+  if (p.variant == 3) {
+    const dim3 pgrid((unsigned)(2 * p.nrb * p.nsplit));
+    hipLaunchKernelGGL(k_vocab_pair<256>, pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb, p.split_len, pS,
+                       pstat, xhdr, (uint64_t*)(xhdr + kPairHdrWords));
+  } else if (p.variant == 1) {
     switch (sl) {
       case 32: hipLaunchKernelGGL(k_vocab32<32>, grid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb, p.split_len, pS, pstat); break;
       case 64: hipLaunchKernelGGL(k_vocab32<64>, grid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb, p.split_len, pS, pstat); break;
@@ -799,7 +1291,7 @@ hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float*
   if (e != hipSuccess) return e;
   if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_vocab_combine, dim3(p.rows), dim3(256), 0, s, p.rows, p.d, p.nsplit, pS,
-                     pstat, max_logit, argmax, conf, lse, selfcond, 1);
+                     pstat, max_logit, argmax, conf, lse, selfcond, 1, xhdr ? xhdr + 8 : nullptr);
   return hipGetLastError();
 }
 
