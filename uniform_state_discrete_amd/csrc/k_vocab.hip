@@ -46,6 +46,16 @@ __device__ __forceinline__ f32x4 mfma16x16(u32x2 a, u32x2 b, f32x4 c) {
 __device__ __forceinline__ void mfma16x32_v(u32x4 a, u32x4 b, f32x4& d) {
   asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
+// The same product without the leading wait states, for operands that no
+// VALU instruction wrote (loaded from memory, constant, or the accumulator of
+// the chain itself), and the first product of a chain, whose accumulator
+// input is the inline constant 0 (no zeroing instructions, no wait states).
+__device__ __forceinline__ void mfma16x32_vn(u32x4 a, u32x4 b, f32x4& d) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16x32_v0(u32x4 a, u32x4 b, f32x4& d) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+}
 // Wait states between the last VGPR-form product and any other reader of its
 // result.
 __device__ __forceinline__ void mfma_v_settle(f32x4 (&lg)[2][2]) {
@@ -940,8 +950,6 @@ __global__ void __launch_bounds__(256, 1)
         // tile t-1's partial logits of this wave (finished last iteration)
 #pragma unroll
         for (int h = 0; h < 4; ++h) xch[w][h][xw] = lg[h];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) lg[h] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       *(DG_LDS u32x2*)(tile + wr_a + 32 * c) = u32x2{e[0], e[1]};
       *(DG_LDS u32x2*)(tile + wr_b + 32 * c) = u32x2{e[2], e[3]};
@@ -953,7 +961,11 @@ __global__ void __launch_bounds__(256, 1)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        mfma16x32_v(e, zf[h][c], lg[h]);
+        // e comes from memory, zf is constant: no VALU write precedes
+        if (c == 0)
+          mfma16x32_v0(e, zf[h][c], lg[h]);  // a new tile's chain starts from 0
+        else
+          mfma16x32_vn(e, zf[h][c], lg[h]);
         stage(c, h);
         __builtin_amdgcn_sched_barrier(0);
       }
