@@ -254,9 +254,8 @@ int dg_denoise_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* 
   hipError_t e;
   if ((e = dg::launch_assemble(dt, R, d, dims->V, io->H, w->E, io->tokens_in, io->selfcond_in, X, s)) != hipSuccess)
     return hip_fail(e, "assemble");
-  if ((e = dg::launch_gemm_nt(dt, R, Hq * dh, d, X, w->Wq, nullptr, Q, s)) != hipSuccess) return hip_fail(e, "Q projection");
-  if ((e = dg::launch_gemm_nt(dt, R, Hkv * dh, d, X, w->Wk, nullptr, Kn, s)) != hipSuccess) return hip_fail(e, "K projection");
-  if ((e = dg::launch_gemm_nt(dt, R, Hkv * dh, d, X, w->Wv, nullptr, Vn, s)) != hipSuccess) return hip_fail(e, "V projection");
+  if ((e = dg::launch_gemm_qkv(dt, R, d, X, w->Wq, Hq * dh, Q, w->Wk, w->Wv, Hkv * dh, Kn, Vn, s)) != hipSuccess)
+    return hip_fail(e, "Q/K/V projections");
   dg::AttnPlan ap = dg::attn_plan(dims->B, dims->C, dims->L, dims->cap, Hq, Hkv, dh, dt, 0);
   if ((e = dg::launch_attn(ap, Q, io->k_cache, io->v_cache, Kn, Vn, O, nullptr, scratch, s,
                            (hipEvent_t)io->ev_attn_begin, (hipEvent_t)io->ev_attn_end)) != hipSuccess)
@@ -299,9 +298,8 @@ int dg_prefill_append(const dg_dims* dims, const dg_weights* w, const void* H,
   hipError_t e;
   if ((e = dg::launch_assemble(dt, R, d, dims->V, H, w->E, tokens_final, nullptr, X, s)) != hipSuccess)
     return hip_fail(e, "assemble");
-  if ((e = dg::launch_gemm_nt(dt, R, Hq * dh, d, X, w->Wq, nullptr, Q, s)) != hipSuccess) return hip_fail(e, "Q projection");
-  if ((e = dg::launch_gemm_nt(dt, R, Hkv * dh, d, X, w->Wk, nullptr, Kn, s)) != hipSuccess) return hip_fail(e, "K projection");
-  if ((e = dg::launch_gemm_nt(dt, R, Hkv * dh, d, X, w->Wv, nullptr, Vn, s)) != hipSuccess) return hip_fail(e, "V projection");
+  if ((e = dg::launch_gemm_qkv(dt, R, d, X, w->Wq, Hq * dh, Q, w->Wk, w->Wv, Hkv * dh, Kn, Vn, s)) != hipSuccess)
+    return hip_fail(e, "Q/K/V projections");
   if ((e = dg::launch_cache_append(dt, dims->B, dims->C, dims->L, dims->cap, Hkv, dh, Kn, k_cache, s)) != hipSuccess)
     return hip_fail(e, "K cache append");
   if ((e = dg::launch_cache_append(dt, dims->B, dims->C, dims->L, dims->cap, Hkv, dh, Vn, v_cache, s)) != hipSuccess)

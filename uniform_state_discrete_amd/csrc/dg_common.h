@@ -88,8 +88,19 @@ hipError_t launch_attn(const AttnPlan& p, const void* q, const void* kc, const v
 hipError_t launch_pack_embedding(int V, int d, const void* E, void* E_tiled, hipStream_t s);
 
 // C[M][N] = A[M][K] . B[N][K]^T (+ Res[M][N]); dtype 0 fp32, 1 bf16.
+// One (weight, residual, output, N) segment of a projection launch.
+struct GemmSeg {
+  const u16* B;
+  const u16* Res;
+  u16* C;
+  int N, tiles;
+};
 hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const void* B,
                           const void* Res, void* C, hipStream_t s);
+// Q, K and V projections of the same activations in one launch (bf16), or
+// three launches (fp32).
+hipError_t launch_gemm_qkv(int dtype, int M, int K, const void* A, const void* Wq, int Nq, void* Q,
+                           const void* Wk, const void* Wv, int Nkv, void* Kn, void* Vn, hipStream_t s);
 
 hipError_t launch_assemble(int dtype, int R, int d, int V, const void* H, const void* E,
                            const int32_t* x, const void* S, void* X, hipStream_t s);

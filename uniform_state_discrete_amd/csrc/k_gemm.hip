@@ -5,61 +5,109 @@
 
 namespace dg {
 
-// bf16 path.  Computed as C^T = B . A^T on 32x32x16 MFMA tiles so that each
-// lane ends up holding 4 consecutive output columns of one output row
-// (8-byte stores).  Workgroup = 4 waves, tile 64 (m) x 64 (n), wave tile
-// 32 x 32; the K loop is double-buffered in registers, 4 K-steps per stage.
-constexpr int GU = 4;  // K-steps of 16 per stage
+// bf16 path.  Workgroup = 4 waves, output tile 64 (m) x 64 (n), wave tile
+// 32 x 32.  K advances in slices of 64 staged through LDS (double-buffered):
+// 8 threads load one 128-byte row segment with 16-byte loads, so every global
+// load instruction reads whole contiguous rows; global loads run four slices
+// (64 KiB per workgroup) ahead of the products, enough bytes in flight to
+// cover the latency of the weight stream from HBM.  Computed as C^T = B . A^T on 32x32x16 MFMA tiles
+// (A operand: weight rows, B operand: activation rows, both read from LDS
+// with one 16-byte read per lane), so each lane ends up holding 4 consecutive
+// output columns of one output row (8-byte stores).  Two accumulators take
+// alternate K-steps: two independent chains keep the matrix core busy.
+// Up to three (weight, output) segments share one launch (the Q, K and V
+// projections read the same activations).
+constexpr int GKS = 64, GLD = GKS + 8;  // K slice; LDS row of 144 bytes: conflict-free
 
-__global__ void __launch_bounds__(256) k_gemm_nt_bf16(int M, int N, int K, const u16* __restrict__ A,
-                                                      const u16* __restrict__ B,
-                                                      const u16* __restrict__ Res,
-                                                      u16* __restrict__ C) {
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, l32 = l & 31;
-  const int m0 = blockIdx.y * 64 + (w >> 1) * 32;
-  const int n0 = blockIdx.x * 64 + (w & 1) * 32;
-  const int am = m0 + l32, bn = n0 + l32;
-  const bool aok = am < M, bok = bn < N;
-  const u16* ap = A + (size_t)(aok ? am : 0) * K + h * 8;
-  const u16* bp = B + (size_t)(bok ? bn : 0) * K + h * 8;
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
-
-  f32x16 acc = zero16();
-  u32x4 xa[GU], wa[GU], xb[GU], wb[GU];
-#pragma unroll
-  for (int u = 0; u < GU; ++u) {
-    xa[u] = aok ? ldg128(ap + u * 16) : z4;
-    wa[u] = bok ? ldg128(bp + u * 16) : z4;
-  }
-  const int KS = 16 * GU;
-  for (int k = 0; k < K; k += 2 * KS) {
-    if (k + KS < K) {
-#pragma unroll
-      for (int u = 0; u < GU; ++u) {
-        xb[u] = aok ? ldg128(ap + k + KS + u * 16) : z4;
-        wb[u] = bok ? ldg128(bp + k + KS + u * 16) : z4;
-      }
+__global__ void __launch_bounds__(256) k_gemm_nt_bf16(int M, int K, const u16* __restrict__ A, GemmSeg s0,
+                                                      GemmSeg s1, GemmSeg s2) {
+  __shared__ __attribute__((aligned(16))) u16 As[2][64][GLD];
+  __shared__ __attribute__((aligned(16))) u16 Bs[2][64][GLD];
+  int tile = blockIdx.x;
+  GemmSeg sg = s0;
+  if (tile >= s0.tiles) {
+    tile -= s0.tiles;
+    sg = s1;
+    if (tile >= s1.tiles) {
+      tile -= s1.tiles;
+      sg = s2;
     }
-#pragma unroll
-    for (int u = 0; u < GU; ++u) acc = mfma32(wa[u], xa[u], acc);
-    if (k + KS >= K) break;
-    if (k + 2 * KS < K) {
-#pragma unroll
-      for (int u = 0; u < GU; ++u) {
-        xa[u] = aok ? ldg128(ap + k + 2 * KS + u * 16) : z4;
-        wa[u] = bok ? ldg128(bp + k + 2 * KS + u * 16) : z4;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < GU; ++u) acc = mfma32(wb[u], xb[u], acc);
   }
-  if (!aok) return;
-  // lane holds C[am][n0 + 8j + 4h + i], i = 0..3
+  const int N = sg.N;
+  const u16* __restrict__ B = sg.B;
+  const int m0 = blockIdx.y * 64, n0 = tile * 64;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
+  const int lr = tid >> 3, lc = (tid & 7) * 8;  // loader: rows lr, lr + 32; columns lc .. lc+7
+  const int nk = K / GKS;                       // K is a multiple of 64
+  // Buffer resources end at the operands: rows past M or N load zeros, with
+  // no branch around the loads.
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(A), (short)0,
+                                                                      (int)((size_t)M * K * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(B), (short)0,
+                                                                      (int)((size_t)N * K * 2), 0x00020000);
+  const uint32_t oa = (uint32_t)(((size_t)(m0 + lr) * K + lc) * 2), ob = (uint32_t)(((size_t)(n0 + lr) * K + lc) * 2);
+  const uint32_t row32 = (uint32_t)(32 * K * 2);
+  constexpr int GPF = 4;         // slices in flight
+  u32x4 ga[GPF][2], gb[GPF][2];  // [slot][row half]
+  auto gload = [&](int slot, int ks) {
+    const uint32_t k2 = (uint32_t)(ks * GKS * 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      ga[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, oa + j * row32 + k2, 0, 0));
+      gb[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob + j * row32 + k2, 0, 0));
+    }
+  };
+  auto lstore = [&](int slot, int buf) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      *(DG_LDS u32x4*)&As[buf][lr + 32 * j][lc] = ga[slot][j];
+      *(DG_LDS u32x4*)&Bs[buf][lr + 32 * j][lc] = gb[slot][j];
+    }
+  };
+  f32x16 acc0 = zero16(), acc1 = zero16();
+  const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
+#pragma unroll
+  for (int s = 0; s < GPF; ++s) gload(s, s);
+  lstore(0, 0);
+  __syncthreads();
+  // one slice: products from LDS buffer (slot & 1), prefetch of slice
+  // ks + GPF into the register slot just emptied, the next slice to LDS
+  auto slice = [&](int u, int ks) {
+    const int buf = u & 1;
+    gload(u, ks + GPF);  // slot u's slice went to LDS in the last iteration
+#pragma unroll
+    for (int kk = 0; kk < GKS / 16; ++kk) {
+      const u32x4 a = *(const DG_LDS u32x4*)&Bs[buf][wn + l32][kk * 16 + 8 * h];
+      const u32x4 b = *(const DG_LDS u32x4*)&As[buf][wm + l32][kk * 16 + 8 * h];
+      if (kk & 1)
+        acc1 = mfma32(a, b, acc1);
+      else
+        acc0 = mfma32(a, b, acc0);
+    }
+    if (ks + 1 < nk) lstore((u + 1) & (GPF - 1), buf ^ 1);
+    __syncthreads();
+  };
+  // unrolled by GPF so that every register slot index is a constant; slices
+  // past the end are loaded (in bounds of the resource) but never stored
+  const int nfull = nk & ~(GPF - 1);
+  for (int ks0 = 0; ks0 < nfull; ks0 += GPF) {
+#pragma unroll
+    for (int u = 0; u < GPF; ++u) slice(u, ks0 + u);
+  }
+#pragma unroll
+  for (int u = 0; u < GPF - 1; ++u)
+    if (nfull + u < nk) slice(u, nfull + u);
+  const int am = m0 + wm + l32;
+  if (am >= M) return;
+  const u16* __restrict__ Res = sg.Res;
+  u16* __restrict__ C = sg.C;
+  // lane holds C[am][n0 + wn + 8j + 4h + i], i = 0..3
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 8 * j + 4 * h;
+    const int n = n0 + wn + 8 * j + 4 * h;
     if (n >= N) continue;
-    float v[4] = {acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+    float v[4] = {acc0[4 * j] + acc1[4 * j], acc0[4 * j + 1] + acc1[4 * j + 1], acc0[4 * j + 2] + acc1[4 * j + 2],
+                  acc0[4 * j + 3] + acc1[4 * j + 3]};
     const size_t o = (size_t)am * N + n;
     if (n + 4 <= N) {
       if (Res) {
@@ -105,18 +153,38 @@ __global__ void __launch_bounds__(256) k_gemm_nt_f32(int M, int N, int K, const 
   }
 }
 
+static GemmSeg gemm_seg(const void* B, const void* Res, void* C, int N) {
+  return GemmSeg{(const u16*)B, (const u16*)Res, (u16*)C, N, (N + 63) / 64};
+}
+
 hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const void* B,
                           const void* Res, void* C, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (dtype == 1) {
-    dim3 grid((N + 63) / 64, (M + 63) / 64);
-    hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, N, K, (const u16*)A,
-                       (const u16*)B, (const u16*)Res, (u16*)C);
+    const GemmSeg s0 = gemm_seg(B, Res, C, N), none = GemmSeg{nullptr, nullptr, nullptr, 0, 0};
+    dim3 grid((unsigned)s0.tiles, (M + 63) / 64);
+    hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, s0, none, none);
   } else {
     dim3 grid((N + 15) / 16, (M + 15) / 16);
     hipLaunchKernelGGL(k_gemm_nt_f32, grid, dim3(256), 0, s, M, N, K, (const float*)A,
                        (const float*)B, (const float*)Res, (float*)C);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_qkv(int dtype, int M, int K, const void* A, const void* Wq, int Nq, void* Q,
+                           const void* Wk, const void* Wv, int Nkv, void* Kn, void* Vn, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (dtype != 1) {
+    hipError_t e = launch_gemm_nt(dtype, M, Nq, K, A, Wq, nullptr, Q, s);
+    if (e == hipSuccess) e = launch_gemm_nt(dtype, M, Nkv, K, A, Wk, nullptr, Kn, s);
+    if (e == hipSuccess) e = launch_gemm_nt(dtype, M, Nkv, K, A, Wv, nullptr, Vn, s);
+    return e;
+  }
+  const GemmSeg sq = gemm_seg(Wq, nullptr, Q, Nq), sk = gemm_seg(Wk, nullptr, Kn, Nkv),
+                sv = gemm_seg(Wv, nullptr, Vn, Nkv);
+  dim3 grid((unsigned)(sq.tiles + sk.tiles + sv.tiles), (M + 63) / 64);
+  hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, sq, sk, sv);
   return hipGetLastError();
 }
 
