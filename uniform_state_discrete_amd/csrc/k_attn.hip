@@ -200,27 +200,48 @@ __global__ void __launch_bounds__(256, 2)
 
 // Merge of the key splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
 // splits in a fixed order (deterministic).  One workgroup per (b, i, h) row.
-__global__ void k_attn_combine_bf16(int nrows, int nsplit, int dh, const float* __restrict__ Opart,
-                                    const float* __restrict__ mpart, const float* __restrict__ lpart,
-                                    u16* __restrict__ O, float* __restrict__ lse_out) {
+constexpr int kAttnMaxSplits = 512;  // attn_plan makes at most 512 splits
+
+__global__ void __launch_bounds__(128) k_attn_combine_bf16(int nrows, int nsplit, int dh,
+                                                           const float* __restrict__ Opart,
+                                                           const float* __restrict__ mpart,
+                                                           const float* __restrict__ lpart,
+                                                           u16* __restrict__ O, float* __restrict__ lse_out) {
+  __shared__ float wgt[kAttnMaxSplits];
+  __shared__ float sh[2];
   const int r = blockIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, mpart[(size_t)s * nrows + r]);
-  float Lt = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = mpart[(size_t)s * nrows + r];
-    if (ms != -INFINITY) Lt += exp2f(ms - M) * lpart[(size_t)s * nrows + r];
-  }
-  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-  for (int f = threadIdx.x; f < dh; f += blockDim.x) {
-    float acc = 0.f;
+  if (threadIdx.x == 0) {
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, mpart[(size_t)s * nrows + r]);
+    float Lt = 0.f;
     for (int s = 0; s < nsplit; ++s) {
       const float ms = mpart[(size_t)s * nrows + r];
-      if (ms != -INFINITY) acc += exp2f(ms - M) * Opart[((size_t)s * nrows + r) * dh + f];
+      const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      wgt[s] = ws;
+      Lt += ws * lpart[(size_t)s * nrows + r];
     }
+    sh[0] = Lt > 0.f ? 1.f / Lt : 0.f;
+    sh[1] = (M + log2f(Lt)) * kLn2;
+  }
+  __syncthreads();
+  const float inv = sh[0];
+  // splits in a fixed order; 8 independent loads in flight per thread
+  for (int f = threadIdx.x; f < dh; f += blockDim.x) {
+    float acc = 0.f;
+    const float* op = Opart + (size_t)r * dh + f;
+    const size_t st = (size_t)nrows * dh;
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = op[(size_t)(s + u) * st];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += wgt[s + u] * v[u];
+    }
+    for (; s < nsplit; ++s) acc += wgt[s] * op[(size_t)s * st];
     O[(size_t)r * dh + f] = (u16)f32_to_bf16(acc * inv);
   }
-  if (lse_out && threadIdx.x == 0) lse_out[r] = (M + log2f(Lt)) * kLn2;
+  if (lse_out && threadIdx.x == 0) lse_out[r] = sh[1];
 }
 
 // ---------------------------------------------------------------------------

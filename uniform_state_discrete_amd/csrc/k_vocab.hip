@@ -624,17 +624,19 @@ constexpr int kPairHdrWords = 64;            // 256 bytes
 constexpr size_t kPairRecBytes = 2 * kPairSlots * 256 * 16;  // per pair
 
 // Exchange record of a lane: its 4 partial logits, each fp32 carrying the
-// slot generation (tile / 4) & 1 in its lowest mantissa bit.  A slot is
-// reused every 4 tiles and a reader is never more than one generation
-// behind, so one bit tells the wanted tile from the one before it; each
-// 4-byte word is single-copy atomic, so a reader accepts the record once all
-// four bits match.  The bit moves a partial by at most one ulp, and both
-// halves add the same tagged values in the same order.  The partners share
-// an XCD: the store (through a buffer resource: no 64-bit lane address)
-// reaches that XCD's L2, the vector L1 being write-through; the load is a
-// device-scope global load, which misses the L1.  (A device-scope buffer
-// load kept returning the L1's stale line on gfx950, in a ping-pong probe
-// between paired workgroups.)
+// slot generation of its tile in its lowest mantissa bit.  A slot is reused
+// every 4 tiles and a reader is never more than one generation behind, so one
+// bit tells the wanted tile from the one before it.  The first generation has
+// bit 1, so a slot that still holds the launch's cleared zeros never matches.
+// Each 4-byte word is single-copy atomic, so a reader accepts the record once
+// all four bits match.  The bit moves a partial by at most one ulp, and both
+// halves add the same tagged values in the same order.  The partners share an
+// XCD: the store (through a buffer resource: no 64-bit lane address) reaches
+// that XCD's L2, the vector L1 being write-through; the load is a device-scope
+// global load, which misses the L1.  (A device-scope buffer load kept
+// returning the L1's stale line on gfx950, in a ping-pong probe between paired
+// workgroups.)
+__device__ __forceinline__ uint32_t pair_gen(int tile) { return (uint32_t)((tile >> 2) + 1) & 1u; }
 __device__ __forceinline__ f32x4 pair_tagged(f32x4 v, uint32_t gen) {
   f32x4 o;
 #pragma unroll
@@ -846,14 +848,14 @@ __global__ void __launch_bounds__(256, 1)
       }
       if (c == 3 && j == 1) own = (own + xa[2]) + xa[3];
       if (c == 3 && j == 2) {
-        own = pair_tagged(own, (uint32_t)((t - 1) >> 2) & 1u);
+        own = pair_tagged(own, pair_gen(t - 1));
         ownb[threadIdx.x] = own;
       }
       if (c == 3 && j == 3 && own_ok)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, own), xrc, xlane,
                                                xo_out + ((t - 1) & 3) * 4096u, 0);
       if (c == 4 && j == 0 && sm_ok) {
-        const uint32_t want = (uint32_t)((t - 2) >> 2) & 1u;  // generation of tile t-2
+        const uint32_t want = pair_gen(t - 2);
         bool ok = pair_gen_ok(xp, want);
         if (!__all(ok) && !broken) {
           if (l == 0) __hip_atomic_fetch_add(&xhdr[9], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1071,7 +1073,18 @@ __global__ void __launch_bounds__(256) k_vocab_combine(int R, int d, int nsplit,
   const float invL = sh[0];
   for (int e = threadIdx.x * 4; e < d; e += 256 * 4) {
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) a += wgt[s] * *(const f32x4*)(pS + ((size_t)s * R + r) * d + e);
+    // splits in a fixed order; 8 independent loads in flight per thread
+    const float* sp = pS + (size_t)r * d + e;
+    const size_t st = (size_t)R * d;
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *(const f32x4*)(sp + (size_t)(s + u) * st);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a += wgt[s + u] * v[u];
+    }
+    for (; s < nsplit; ++s) a += wgt[s] * *(const f32x4*)(sp + (size_t)s * st);
     a *= invL;
     if (out_bf16) {
       u32x2 o = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
