@@ -210,18 +210,24 @@ __global__ void __launch_bounds__(128) k_attn_combine_bf16(int nrows, int nsplit
   __shared__ float wgt[kAttnMaxSplits];
   __shared__ float sh[2];
   const int r = blockIdx.x;
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {
+    // one wave: lane l takes splits l, l+64, ...; fixed-pattern reductions
+    const int l = threadIdx.x;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, mpart[(size_t)s * nrows + r]);
-    float Lt = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
+    for (int s = l; s < nsplit; s += 64) M = fmaxf(M, mpart[(size_t)s * nrows + r]);
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float part = 0.f;
+    for (int s = l; s < nsplit; s += 64) {
       const float ms = mpart[(size_t)s * nrows + r];
       const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
       wgt[s] = ws;
-      Lt += ws * lpart[(size_t)s * nrows + r];
+      part += ws == 0.f ? 0.f : ws * lpart[(size_t)s * nrows + r];
     }
-    sh[0] = Lt > 0.f ? 1.f / Lt : 0.f;
-    sh[1] = (M + log2f(Lt)) * kLn2;
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    if (l == 0) {
+      sh[0] = part > 0.f ? 1.f / part : 0.f;
+      sh[1] = (M + log2f(part)) * kLn2;
+    }
   }
   __syncthreads();
   const float inv = sh[0];
@@ -236,9 +242,9 @@ __global__ void __launch_bounds__(128) k_attn_combine_bf16(int nrows, int nsplit
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = op[(size_t)(s + u) * st];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc += wgt[s + u] * v[u];
+      for (int u = 0; u < 8; ++u) acc += wgt[s + u] == 0.f ? 0.f : wgt[s + u] * v[u];
     }
-    for (; s < nsplit; ++s) acc += wgt[s] * op[(size_t)s * st];
+    for (; s < nsplit; ++s) acc += wgt[s] == 0.f ? 0.f : wgt[s] * op[(size_t)s * st];
     O[(size_t)r * dh + f] = (u16)f32_to_bf16(acc * inv);
   }
   if (lse_out && threadIdx.x == 0) lse_out[r] = sh[1];

@@ -1048,26 +1048,43 @@ __global__ void __launch_bounds__(256) k_vocab_combine(int R, int d, int nsplit,
     }
     return;
   }
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {
+    // one wave: lane l takes splits l, l+64, ... (independent loads), then
+    // fixed-pattern reductions across the wave
+    const int l = threadIdx.x;
     float M = -INFINITY, mu = -INFINITY;
-    int A = 0;
-    for (int s = 0; s < nsplit; ++s) {
+    int A = 0, Sfirst = 0x7FFFFFFF;
+    for (int s = l; s < nsplit; s += 64) {
       const f32x4 st = pstat[(size_t)s * R + r];
-      if (st[2] > M) { M = st[2]; A = __float_as_int(st[3]); }
+      if (st[2] > M) { M = st[2]; A = __float_as_int(st[3]); Sfirst = s; }
       mu = fmaxf(mu, st[0]);
     }
-    float Lt = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
+    // max logit; argmax of the first (lowest-id) split attaining it
+    for (int o = 32; o > 0; o >>= 1) {
+      const float oM = __shfl_xor(M, o);
+      const int oA = __shfl_xor(A, o), oS = __shfl_xor(Sfirst, o);
+      const bool take = (oM > M) | ((oM == M) & (oS < Sfirst));
+      M = take ? oM : M;
+      A = take ? oA : A;
+      Sfirst = take ? oS : Sfirst;
+      mu = fmaxf(mu, __shfl_xor(mu, o));
+    }
+    float part = 0.f;
+    for (int s = l; s < nsplit; s += 64) {
       const f32x4 st = pstat[(size_t)s * R + r];
       const float ws = st[0] == -INFINITY ? 0.f : expf(st[0] - mu);
       wgt[s] = ws;
-      Lt += ws * st[1];
+      part += ws * st[1];
     }
-    sh[0] = 1.f / Lt;
-    max_logit[r] = M;
-    argmax[r] = A;
-    conf[r] = expf(M - mu) / Lt;
-    if (lse) lse[r] = mu + logf(Lt);
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    const float Lt = part;
+    if (l == 0) {
+      sh[0] = 1.f / Lt;
+      max_logit[r] = M;
+      argmax[r] = A;
+      conf[r] = expf(M - mu) / Lt;
+      if (lse) lse[r] = mu + logf(Lt);
+    }
   }
   __syncthreads();
   const float invL = sh[0];
