@@ -118,38 +118,50 @@ __global__ void __launch_bounds__(256, 2)
         sacc[kb] = mfma32(ka, qf[ks], sacc[kb]);
       }
     }
+    // scores stay unscaled: p = 2^(s sl2 - m) with m in the scaled (log2) domain
+    if (!(t0 + 64 <= k_end && (!causal || t0 + 63 <= L))) {
+      // a ragged or causal tile (uniform branch): masked keys get -inf
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = t0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+          const bool valid = key < k_end && (!causal || key <= qlim);
+          sacc[kb][e] = valid ? sacc[kb][e] : -INFINITY;
+        }
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = t0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-        const bool valid = key < k_end && (!causal || key <= qlim);
-        const float s = valid ? sacc[kb][e] * sl2 : -INFINITY;
-        sacc[kb][e] = s;
-        tmax = fmaxf(tmax, s);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(sacc[kb][e], sacc[kb][e + 1]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;  // sl2 > 0 keeps the order
     const float mnew = fmaxf(m, tmax);
     if (mnew > m) {
-      const float alpha = exp2f(m - mnew);  // m = -inf gives 0
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // m = -inf gives 0
       lsum *= alpha;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
       m = mnew;
     }
+    // a row with no valid key yet keeps m = -inf: its scores are all -inf
+    const float mu = m == -INFINITY ? 0.f : m;
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    typedef float f32x2v __attribute__((ext_vector_type(2)));
     u32x4 pf[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float pv[8];
+      uint32_t pk[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float s = sacc[q >> 1][8 * (q & 1) + e];
-        pv[e] = (s == -INFINITY) ? 0.f : round_bf16(exp2f(s - m));
-        lsum += pv[e];
+      for (int e = 0; e < 8; e += 2) {
+        const float s0 = sacc[q >> 1][8 * (q & 1) + e], s1 = sacc[q >> 1][8 * (q & 1) + e + 1];
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s0, sl2, -mu)), p1 = __builtin_amdgcn_exp2f(fmaf(s1, sl2, -mu));
+        // P enters the product in bf16: the normaliser sums the same rounded values
+        const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{p0, p1}, bf16x2v));
+        lsum += __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
+        pk[e >> 1] = u;
       }
-      pf[q] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                    pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+      pf[q] = u32x4{pk[0], pk[1], pk[2], pk[3]};
     }
     const DG_LDS u16* vbase = (const DG_LDS u16*)&Vs[buf][0][0];
 #pragma unroll
