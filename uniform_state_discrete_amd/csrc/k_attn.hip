@@ -70,8 +70,10 @@ __global__ void __launch_bounds__(256, 2)
     for (int u = 0; u < NLD; ++u) {
       const int idx = threadIdx.x + u * 256;
       const int rr = idx / CPR, cc = (idx % CPR) * 8;
-      const int key = t0 + rr;
-      const bool ok = key < k_end;
+      // keys past the split load a valid key's row instead (finite data; the
+      // scores of those keys are masked, so their P is 0): no select on the
+      // loaded value, which would wait for the load right here
+      const int key = min(t0 + rr, k_end - 1);
       size_t o;
       const u16 *kp, *vp;
       if (key < L) {
@@ -79,12 +81,12 @@ __global__ void __launch_bounds__(256, 2)
         kp = Kc + o;
         vp = Vc + o;
       } else {
-        o = (((size_t)b * C + (ok ? key - L : 0)) * Hkv + g) * DH + cc;
+        o = (((size_t)b * C + (key - L)) * Hkv + g) * DH + cc;
         kp = Kn + o;
         vp = Vn + o;
       }
-      kreg[u] = ok ? ldg128(kp) : z4;
-      vreg[u] = ok ? ldg128(vp) : z4;
+      kreg[u] = ldg128(kp);
+      vreg[u] = ldg128(vp);
     }
   };
   auto store_tile = [&](int buf) {
@@ -108,14 +110,22 @@ __global__ void __launch_bounds__(256, 2)
     const int t0 = k_begin + t * 64;
     if (t + 1 < ntiles) load_tile(t0 + 64);
 
-    f32x16 sacc[2];
+    // S^T for keys 0..31 and 32..63: two independent chains interleaved, K
+    // fragments read two steps ahead of their products
+    f32x16 sacc[2] = {zero16(), zero16()};
+    {
+      u32x4 ka[3][2];
+      auto kread = [&](int ks) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = zero16();
+        for (int kb = 0; kb < 2; ++kb) ka[ks % 3][kb] = *(const u32x4*)&Ks[buf][kb * 32 + l32][ks * 16 + h * 8];
+      };
+      kread(0);
+      kread(1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 ka = *(const u32x4*)&Ks[buf][kb * 32 + l32][ks * 16 + h * 8];
-        sacc[kb] = mfma32(ka, qf[ks], sacc[kb]);
+        if (ks + 2 < KS) kread(ks + 2);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(ka[ks % 3][kb], qf[ks], sacc[kb]);
       }
     }
     // scores stay unscaled: p = 2^(s sl2 - m) with m in the scaled (log2) domain
@@ -163,17 +173,29 @@ __global__ void __launch_bounds__(256, 2)
       }
       pf[q] = u32x4{pk[0], pk[1], pk[2], pk[3]};
     }
+    // O^T += V^T P^T: the MB output chains interleaved, V^T fragments of the
+    // next key group read one step ahead of their products
     const DG_LDS u16* vbase = (const DG_LDS u16*)&Vs[buf][0][0];
+    {
+      u32x4 va[2][MB];
+      auto vread = [&](int q) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r0 = 16 * q + 4 * h + ((l & 15) >> 2);
+          const int c0 = mb * 32 + 16 * ((l >> 4) & 1) + (l & 3) * 4;
+          const u32x2 a0 = lds_read_tr16(vbase + r0 * VP + c0);
+          const u32x2 a1 = lds_read_tr16(vbase + (r0 + 8) * VP + c0);
+          va[q & 1][mb] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        }
+      };
+      vread(0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r0 = 16 * q + 4 * h + ((l & 15) >> 2);
-        const int c0 = mb * 32 + 16 * ((l >> 4) & 1) + (l & 3) * 4;
-        const u32x2 a0 = lds_read_tr16(vbase + r0 * VP + c0);
-        const u32x2 a1 = lds_read_tr16(vbase + (r0 + 8) * VP + c0);
-        oacc[mb] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf[q], oacc[mb]);
+        if (q + 1 < 4) vread(q + 1);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb] = mfma32(va[q & 1][mb], pf[q], oacc[mb]);
       }
+    }
     if (t + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();
   }
