@@ -23,6 +23,8 @@ namespace dg {
 // barrier per tile.  Rows of the K tile are padded by 16 B and of the V tile
 // by 64 B so that the row-wise and the transposing reads are conflict-free.
 // ---------------------------------------------------------------------------
+constexpr float kAttnLazy = 8.0f;
+
 template <int DH>
 __global__ void __launch_bounds__(256, 2)
     k_attn_bf16(int B, int C, int L, int cap, int Hq, int Hkv, int G, int causal, int nrb,
@@ -146,13 +148,15 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(sacc[kb][e], sacc[kb][e + 1]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;  // sl2 > 0 keeps the order
-    const float mnew = fmaxf(m, tmax);
-    if (mnew > m) {
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // m = -inf gives 0
+    // Lazy reference: it moves only when a score exceeds it by more than
+    // kAttnLazy (log2 units), so p <= 2^kAttnLazy and the accumulators are
+    // rescaled a few times per row instead of on most tiles.
+    if (tmax > m + kAttnLazy) {
+      const float alpha = __builtin_amdgcn_exp2f(m - tmax);  // m = -inf gives 0
       lsum *= alpha;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
-      m = mnew;
+      m = tmax;
     }
     // a row with no valid key yet keeps m = -inf: its scores are all -inf
     const float mu = m == -INFINITY ? 0.f : m;
