@@ -126,7 +126,9 @@ int dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_step_io *
  * j < L + i + 1 (prefill of a block after an L-row cache).
  * q[B][C][Hq][dh], k_new/v_new[B][C][Hkv][dh], caches as in dg_step_io,
  * out[B][C][Hq][dh]; lse_out[B][C][Hq] (natural log, float32) may be NULL.
- * Only dims->{B,C,L,cap,n_q_heads,n_kv_heads,head_dim,dtype} are used. */
+ * Only dims->{B,C,L,cap,n_q_heads,n_kv_heads,head_dim,dtype} are used.
+ * bf16 needs head_dim 64 or 128 and cap * head_dim * 2 < 2^31 (one cache
+ * slab is addressed with 32-bit offsets); otherwise DG_EUNSUPPORTED. */
 size_t dg_attn_workspace_bytes(const dg_dims *dims);
 int dg_attn_bidir(const dg_dims *dims, const void *q, const void *k_cache, const void *v_cache,
                   const void *k_new, const void *v_new, void *out, float *lse_out, int causal,

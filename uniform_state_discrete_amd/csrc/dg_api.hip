@@ -46,6 +46,8 @@ int check_dims(const dg_dims* d, bool need_vocab) {
   if (d->dtype == DG_BF16) {
     if (d->head_dim != 64 && d->head_dim != 128) return fail(DG_EUNSUPPORTED, "bf16 head_dim must be 64 or 128 (got %d)", d->head_dim);
     if (d->n_kv_heads * d->head_dim % 64) return fail(DG_EUNSUPPORTED, "bf16 needs n_kv_heads*head_dim %% 64 == 0");
+    if ((size_t)d->cap * d->head_dim * 2 > 0x7FFFFFFFu)
+      return fail(DG_EUNSUPPORTED, "bf16 cache slab of one (canvas, KV head) must be under 2 GiB (cap=%d)", d->cap);
   } else {
     if (d->head_dim > 256) return fail(DG_EUNSUPPORTED, "fp32 head_dim must be <= 256 (got %d)", d->head_dim);
   }

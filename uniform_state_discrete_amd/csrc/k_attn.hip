@@ -38,7 +38,12 @@ __global__ void __launch_bounds__(256, 2)
   __shared__ __attribute__((aligned(16))) u16 Vs[2][64][VP];
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, l32 = l & 31;
-  int bid = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs in turn, each with its own L2.  The
+  // logical order puts the nrb row blocks that read the same keys next to
+  // each other on one XCD, so the K/V tiles come from that XCD's L2 after the
+  // first of them has fetched it.  The grid is padded to a multiple of 8.
+  int bid = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  if (bid >= nrb * nsplit * Hkv * B) return;
   const int rb = bid % nrb;
   bid /= nrb;
   const int split = bid % nsplit;
@@ -67,7 +72,26 @@ __global__ void __launch_bounds__(256, 2)
   const int qlim = L + qi;  // causal: key <= L + i
 
   u32x4 kreg[NLD], vreg[NLD];
+  // Tiles that lie in the cache and inside the split (all but the last one
+  // or two) load through buffer resources over this (b, g) cache slab: a
+  // fixed per-lane offset plus a scalar tile offset, no address arithmetic.
+  constexpr int RPU = 256 / CPR;  // tile rows per load instruction
+  const int kfast = min(L, k_end);
+  const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(Kc + ((size_t)b * Hkv + g) * cap * DH), (short)0, (int)((size_t)cap * DH * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsV = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(Vc + ((size_t)b * Hkv + g) * cap * DH), (short)0, (int)((size_t)cap * DH * 2), 0x00020000);
+  const uint32_t voff = (uint32_t)(((threadIdx.x / CPR) * DH + (threadIdx.x % CPR) * 8) * 2);
   auto load_tile = [&](int t0) {
+    if (t0 + 64 <= kfast) {
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) {
+        const uint32_t so = (uint32_t)((t0 + u * RPU) * DH * 2);
+        kreg[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voff, so, 0));
+        vreg[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voff, so, 0));
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int idx = threadIdx.x + u * 256;
@@ -106,6 +130,12 @@ __global__ void __launch_bounds__(256, 2)
     load_tile(k_begin);
     store_tile(0);
   }
+  // The Q fragments are complete on every path into the loop.  Without this
+  // use, the path with no tiles leaves their loads pending at the loop head,
+  // and the first product of every tile would then wait for all vector
+  // loads, including the K/V prefetch issued just before it.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
@@ -162,6 +192,7 @@ __global__ void __launch_bounds__(256, 2)
     const float mu = m == -INFINITY ? 0.f : m;
     typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
     typedef float f32x2v __attribute__((ext_vector_type(2)));
+    const bf16x2v one2 = __builtin_bit_cast(bf16x2v, 0x3f803f80u);  // (1, 1)
     u32x4 pf[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -170,10 +201,11 @@ __global__ void __launch_bounds__(256, 2)
       for (int e = 0; e < 8; e += 2) {
         const float s0 = sacc[q >> 1][8 * (q & 1) + e], s1 = sacc[q >> 1][8 * (q & 1) + e + 1];
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s0, sl2, -mu)), p1 = __builtin_amdgcn_exp2f(fmaf(s1, sl2, -mu));
-        // P enters the product in bf16: the normaliser sums the same rounded values
-        const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{p0, p1}, bf16x2v));
-        lsum += __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
-        pk[e >> 1] = u;
+        // P enters the product in bf16: the normaliser sums the same rounded
+        // values (a dot product of the packed pair with (1, 1))
+        const bf16x2v pb = __builtin_convertvector(f32x2v{p0, p1}, bf16x2v);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, one2, lsum, false);
+        pk[e >> 1] = __builtin_bit_cast(uint32_t, pb);
       }
       pf[q] = u32x4{pk[0], pk[1], pk[2], pk[3]};
     }
@@ -402,7 +434,7 @@ hipError_t launch_attn(const AttnPlan& p, const void* q, const void* kc, const v
   float* Opart = (float*)ws;
   float* mpart = Opart + (size_t)p.nsplit * nrows * p.dh;
   float* lpart = mpart + (size_t)p.nsplit * nrows;
-  const dim3 grid((unsigned)(p.nrb * p.nsplit * p.Hkv * p.B));
+  const dim3 grid((unsigned)((p.nrb * p.nsplit * p.Hkv * p.B + 7) / 8 * 8));
 #define DG_ATTN_LAUNCH(DHV)                                                                       \
   hipLaunchKernelGGL(k_attn_bf16<DHV>, grid, dim3(256), 0, s, p.B, p.C, p.L, p.cap, p.Hq, p.Hkv, \
                      G, p.causal, p.nrb, p.nsplit, p.keys_per_split, (const u16*)q,                \
