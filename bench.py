@@ -92,6 +92,41 @@ def cpu_baseline(p, cfg, min_seconds=10.0):
             "sample": f"{n} whole numpy fp64 oracle step(s) of {cfg.name}, chained, {el:.1f} s"}
 
 
+def attention_hbm_shape(stream, reps=20):
+    """The HBM-bound attention shape: the long-context cache (32768 rows, 8
+    KV heads of 128, K/V ~ N(0, 1), bf16) read by 16 canvas queries of 32
+    heads, so 64 query rows per KV head and about 64 flop per cache byte, far
+    below the ridge.  Times dg_attn_bidir (attention kernel + split combine)
+    with HIP events on the launch stream; returns the cache bytes streamed per
+    second against the HBM peak."""
+    import torch
+    import uniform_state_discrete_amd as dg
+    B, C, L, Hq, Hkv, dh = 1, 16, 32768, 32, 8, 128
+    g = torch.Generator(device="cuda").manual_seed(3003)
+    rnd = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    Kc, Vc = rnd(B, Hkv, L + C, dh), rnd(B, Hkv, L + C, dh)
+    q, kn, vn = rnd(B, C, Hq, dh), rnd(B, C, Hkv, dh), rnd(B, C, Hkv, dh)
+    out = torch.empty_like(q)
+    dims = dg.make_dims(B, C, L, L + C, 4096, Hq, Hkv, dh, 0, dg.DG_BF16)
+    ws = dg.workspace(dg.dg_attn_workspace_bytes(dims))
+    for _ in range(3):
+        dg.dg_attn_bidir(dims, q, Kc, Vc, kn, vn, out, None, 0, ws, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        dg.dg_attn_bidir(dims, q, Kc, Vc, kn, vn, out, None, 0, ws, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    by = 2.0 * B * L * Hkv * dh * 2
+    fl = 4.0 * B * C * (L + C) * Hq * dh
+    return {"shape": f"canvas {C} x {Hq} heads over a {L}-row cache, {Hkv} KV heads, head_dim {dh}, bf16",
+            "us": round(us, 2), "cache_bytes": by, "achieved_GBs": round(by / us / 1e3, 1),
+            "hbm_frac": round(by / us / 1e3 / PEAK_HBM_GBS, 4),
+            "mfma_frac": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+
+
 def copy_calibration(mib):
     """A plain device-to-device copy of known size, for scaling HBM counters."""
     import torch
@@ -111,6 +146,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attn-hbm", action="store_true", help="skip the HBM-bound attention shape")
     ap.add_argument("--copy-mib", type=int, default=0, help="only run a plain copy of this size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -224,6 +260,8 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                      "algorithmic_bytes": alg["by_E"] + cfg.B * cfg.C * cfg.d * 2.0},
     }
+    if not args.no_attn_hbm:
+        out["attention_hbm_shape"] = attention_hbm_shape(stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, cfg)
     print(json.dumps(out), flush=True)
