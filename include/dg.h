@@ -189,6 +189,57 @@ int dg_prefill_append(const dg_dims *dims, const dg_weights *w, const void *H,
                       const int32_t *tokens_final, void *k_cache, void *v_cache, void *attn_out,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* Block diffusion ("Campionamento multi-canvas (diffusione a blocchi)"):
+ * `blocks` canvases diffused one after another, each for `steps` denoise
+ * steps and then appended to the KV cache by the causal prefill
+ * ("Architettura: il prefill incrementale e il denoising").  For block k
+ * (cache length L_k = dims->L + k C):
+ *   canvas = dg_init_canvas(draw 0 of block k)
+ *   for s in 0..steps-1: dg_denoise_step(tau = taus[s], t = s + 1, block = k,
+ *       cache length L_k; the first step reads no self-conditioning vector)
+ *   tokens[k] = argmax of the last step (the finished canvas, not renoised)
+ *   dg_prefill_append(H[k], tokens[k]): cache rows [L_k, L_k + C) are written
+ * Needs dims->cap >= dims->L + blocks C.  Every pointer is a caller-owned
+ * device pointer; R = B C. */
+typedef struct {
+  const void *H;            /* [blocks][B][C][d] hidden rows of each block's canvas */
+  void *k_cache, *v_cache;  /* [B][Hkv][cap][dh]; rows [0, L) valid on entry */
+  int32_t *tokens;          /* [blocks][B][C] finished canvas of every block */
+  int32_t *canvas;          /* [2][B][C] working canvases; the initial canvas of a
+                               block is drawn into the first [B][C] (with
+                               trace_tokens set only that part is used) */
+  void *selfcond;           /* [2][B][C][d] working self-conditioning vectors
+                               (unused when trace_selfcond is set) */
+  float *max_logit, *conf;  /* [R] statistics of the latest step (conf unused when trace_conf is set) */
+  int32_t *argmax;          /* [R] argmax of the latest step but the last of a block */
+  uint8_t *mask;            /* [R] renoise mask of the latest step; may be NULL */
+  /* Optional per-step records (NULL: not kept).  When set, each step writes
+   * its outputs there and the next step reads them from there. */
+  int32_t *trace_tokens;    /* [blocks][steps][B][C] tokens after each step */
+  float *trace_conf;        /* [blocks][steps][R] confidence of each step */
+  void *trace_selfcond;     /* [blocks][steps][B][C][d] S of each step */
+} dg_block_io;
+
+/* Enqueues the whole block loop on `stream`.  taus is a HOST array of
+ * `steps` thresholds, read during the call.  ws: dg_workspace_bytes(dims). */
+int dg_block_loop(const dg_dims *dims, const dg_weights *w, const dg_block_io *io,
+                  const float *taus, int32_t steps, int32_t blocks, uint64_t seed,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* The same sequence captured once into an instantiated HIP graph, replayed
+ * with dg_graph_launch: one launch per whole sequence instead of one per
+ * kernel.  The graph holds the pointers and scalars of the capture call, so
+ * every buffer must stay allocated until dg_graph_destroy.  stream must be a
+ * created stream (not NULL): capture runs on it, nothing executes during the
+ * capture.  On failure *graph is NULL and nothing was launched.  Replays on
+ * one graph must not overlap (they share the workspace). */
+typedef struct dg_graph_s *dg_graph;
+int dg_graph_capture_block_loop(const dg_dims *dims, const dg_weights *w, const dg_block_io *io,
+                                const float *taus, int32_t steps, int32_t blocks, uint64_t seed,
+                                void *ws, size_t ws_bytes, void *stream, dg_graph *graph);
+int dg_graph_launch(dg_graph graph, void *stream);
+void dg_graph_destroy(dg_graph graph);
+
 /* Text of a dg_status; text of the last failure on the calling thread. */
 const char *dg_status_str(int status);
 const char *dg_last_error(void);

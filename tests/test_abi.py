@@ -140,3 +140,36 @@ def test_tiled_embedding_sizes_and_checks(L):
     assert lib.dg_pack_embedding(100, 64, L.DG_BF16, vp(FAKE), vp(FAKE + 8), None) == L.DG_EINVAL  # aligned
     assert lib.dg_pack_embedding(100, 64, L.DG_BF16, vp(FAKE), vp(FAKE + 4096), None) == L.DG_EINVAL  # overlap
     assert b"overlap" in lib.dg_last_error()
+
+
+def test_block_loop_and_graph_argument_checks(L):
+    lib = L.lib()
+    w = L.Weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    io = L.BlockIO(*[FAKE if k not in ("mask", "trace_tokens", "trace_conf", "trace_selfcond") else None
+                     for k in L.BLOCK_IO_FIELDS])
+    taus = (ctypes.c_float * 4)(0.5, 0.6, 0.7, 0.8)
+    tp = ctypes.cast(taus, ctypes.c_void_p)
+    # the cache has no room for the appended blocks
+    st = lib.dg_block_loop(ctypes.byref(dims(L=1024, cap=1024 + 256)), ctypes.byref(w), ctypes.byref(io),
+                           tp, 4, 2, 1, FAKE, 1 << 40, None)
+    assert st == L.DG_EINVAL and b"cap" in lib.dg_last_error()
+    d = dims(L=1024, cap=1024 + 2 * 256)
+    assert lib.dg_block_loop(ctypes.byref(d), ctypes.byref(w), ctypes.byref(io), tp, 0, 2, 1, FAKE, 1 << 40,
+                             None) == L.DG_EINVAL
+    assert lib.dg_block_loop(ctypes.byref(d), ctypes.byref(w), ctypes.byref(io), None, 4, 2, 1, FAKE, 1 << 40,
+                             None) == L.DG_EINVAL
+    assert lib.dg_block_loop(ctypes.byref(d), ctypes.byref(w), ctypes.byref(io), tp, 4, 2, 1, FAKE, 1000,
+                             None) == L.DG_EWORKSPACE
+    io_nocanvas = L.BlockIO(*[FAKE if k not in ("canvas", "mask", "trace_tokens", "trace_conf", "trace_selfcond")
+                              else None for k in L.BLOCK_IO_FIELDS])
+    assert lib.dg_block_loop(ctypes.byref(d), ctypes.byref(w), ctypes.byref(io_nocanvas), tp, 4, 2, 1, FAKE,
+                             1 << 40, None) == L.DG_EINVAL
+    # graph capture needs a created stream and an output handle
+    h = ctypes.c_void_p(FAKE)
+    st = lib.dg_graph_capture_block_loop(ctypes.byref(d), ctypes.byref(w), ctypes.byref(io), tp, 4, 2, 1,
+                                         FAKE, 1 << 40, None, ctypes.byref(h))
+    assert st == L.DG_EINVAL and h.value is None and b"stream" in lib.dg_last_error()
+    assert lib.dg_graph_capture_block_loop(ctypes.byref(d), ctypes.byref(w), ctypes.byref(io), tp, 4, 2, 1,
+                                           FAKE, 1 << 40, FAKE, None) == L.DG_EINVAL
+    assert lib.dg_graph_launch(None, None) == L.DG_EINVAL
+    lib.dg_graph_destroy(None)

@@ -47,6 +47,14 @@ class StepIO(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in STEP_IO_FIELDS]
 
 
+BLOCK_IO_FIELDS = ("H", "k_cache", "v_cache", "tokens", "canvas", "selfcond", "max_logit", "conf",
+                   "argmax", "mask", "trace_tokens", "trace_conf", "trace_selfcond")
+
+
+class BlockIO(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_IO_FIELDS]
+
+
 _lib = None
 
 
@@ -77,6 +85,13 @@ def lib():
             "dg_init_canvas": (ctypes.c_int, [i32, i32, i32, u64, u32, vp, vp]),
             "dg_prefill_append": (ctypes.c_int, [pd, ctypes.POINTER(Weights), vp, vp, vp, vp, vp,
                                                  vp, sz, vp]),
+            "dg_block_loop": (ctypes.c_int, [pd, ctypes.POINTER(Weights), ctypes.POINTER(BlockIO), vp,
+                                             i32, i32, u64, vp, sz, vp]),
+            "dg_graph_capture_block_loop": (ctypes.c_int, [pd, ctypes.POINTER(Weights), ctypes.POINTER(BlockIO),
+                                                           vp, i32, i32, u64, vp, sz, vp,
+                                                           ctypes.POINTER(ctypes.c_void_p)]),
+            "dg_graph_launch": (ctypes.c_int, [vp, vp]),
+            "dg_graph_destroy": (None, [vp]),
             "dg_status_str": (ctypes.c_char_p, [ctypes.c_int]),
             "dg_last_error": (ctypes.c_char_p, []),
         }
@@ -243,3 +258,63 @@ def dg_prefill_append(dims, weights, H, tokens_final, k_cache, v_cache, attn_out
                                  ptr(k_cache), ptr(v_cache), ptr(attn_out), ptr(ws),
                                  ws.numel() if ws is not None else 0, stream_handle(stream))
     _check(st, "dg_prefill_append")
+
+
+def _block_args(dims, weights, io, taus, steps):
+    _check_float_dtype(dims, [(k, weights.get(k)) for k in WEIGHT_FIELDS] +
+                       [(k, io.get(k)) for k in ("H", "k_cache", "v_cache", "selfcond", "trace_selfcond")])
+    for k in ("tokens", "canvas", "argmax", "trace_tokens"):
+        if io.get(k) is not None and io[k].dtype != torch.int32:
+            raise TypeError(f"{k}: expected torch.int32")
+    if len(taus) != steps:
+        raise ValueError(f"need {steps} thresholds, got {len(taus)}")
+    w = Weights(*(ptr(weights.get(k)) for k in WEIGHT_FIELDS))
+    b = BlockIO(*(ptr(io.get(k)) for k in BLOCK_IO_FIELDS))
+    t = (ctypes.c_float * steps)(*[float(x) for x in taus])
+    return w, b, t
+
+
+def dg_block_loop(dims, weights, io, taus, steps, blocks, seed, ws, stream=None):
+    """io: dict with the dg_block_io fields (missing keys -> NULL); taus: the
+    `steps` thresholds of a block (host floats)."""
+    w, b, t = _block_args(dims, weights, io, taus, steps)
+    st = lib().dg_block_loop(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(b), ctypes.cast(t, ctypes.c_void_p),
+                             int(steps), int(blocks), int(seed), ptr(ws), ws.numel() if ws is not None else 0,
+                             stream_handle(stream))
+    _check(st, "dg_block_loop")
+
+
+class Graph:
+    """An instantiated HIP graph of the block loop (dg_graph).  Holds the
+    tensors it was captured on, so they outlive it."""
+
+    def __init__(self, handle, keep):
+        self._h = handle
+        self._keep = keep
+
+    def launch(self, stream=None):
+        _check(lib().dg_graph_launch(self._h, stream_handle(stream)), "dg_graph_launch")
+
+    def close(self):
+        if self._h:
+            lib().dg_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def dg_graph_capture_block_loop(dims, weights, io, taus, steps, blocks, seed, ws, stream):
+    """Capture the block loop on `stream` (a torch.cuda.Stream, not the NULL
+    stream) into a Graph; nothing runs until Graph.launch."""
+    w, b, t = _block_args(dims, weights, io, taus, steps)
+    h = ctypes.c_void_p()
+    st = lib().dg_graph_capture_block_loop(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(b),
+                                           ctypes.cast(t, ctypes.c_void_p), int(steps), int(blocks), int(seed),
+                                           ptr(ws), ws.numel() if ws is not None else 0, stream_handle(stream),
+                                           ctypes.byref(h))
+    _check(st, "dg_graph_capture_block_loop")
+    return Graph(h.value, (dict(weights), dict(io), ws))

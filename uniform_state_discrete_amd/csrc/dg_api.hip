@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <new>
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -116,7 +118,192 @@ int check_bf16_align(const dg_dims* d, const void* const* ptrs, int n) {
 
 char* at(void* ws, size_t off) { return (char*)ws + off; }
 
+int check_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io, const void* ws,
+               size_t ws_bytes) {
+  int st = check_dims(dims, true);
+  if (st != DG_OK) return st;
+  if (!w || !io) return fail(DG_EINVAL, "weights and io must be non-NULL");
+  if (!w->Wq || !w->Wk || !w->Wv || !w->Wo || !w->E || (dims->dtype == DG_BF16 && !w->E_tiled))
+    return fail(DG_EINVAL, "every weight pointer (and E_tiled for bf16) must be non-NULL");
+  if (!io->H || !io->tokens_in || !io->tokens_out || !io->selfcond_out || !io->max_logit ||
+      !io->conf || !io->argmax || (dims->L > 0 && (!io->k_cache || !io->v_cache)))
+    return fail(DG_EINVAL, "H, tokens_in/out, selfcond_out, max_logit, conf, argmax (and the caches when L > 0) must be non-NULL");
+  const int R = dims->B * dims->C;
+  if ((st = check_vocab_shape(R, dims->d, dims->V, dims->dtype)) != DG_OK) return st;
+  if (dims->dtype == DG_BF16 && (dims->d % 128 || dims->n_q_heads * dims->head_dim % 64))
+    return fail(DG_EUNSUPPORTED, "bf16 step needs d %% 128 == 0 and n_q_heads*head_dim %% 64 == 0");
+  const void* ptrs[] = {w->Wq, w->Wk, w->Wv, w->Wo, w->E, io->H, io->k_cache, io->v_cache,
+                        io->selfcond_in, io->selfcond_out, io->x_out, io->q_out, io->k_new_out,
+                        io->v_new_out, io->attn_out, io->z_out, w->E_tiled};
+  if ((st = check_bf16_align(dims, ptrs, 17)) != DG_OK) return st;
+  const StepLayout L = step_layout(dims);
+  if (!ws || ws_bytes < L.total)
+    return fail(DG_EWORKSPACE, "step workspace needs %zu bytes (got %zu)", L.total, ws ? ws_bytes : 0);
+  if (!aligned16(ws)) return fail(DG_EINVAL, "workspace must be 16-byte aligned");
+  return DG_OK;
+}
+
+int enqueue_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io, float tau,
+                 uint64_t seed, uint32_t t, uint32_t block, void* ws, hipStream_t s) {
+  const StepLayout L = step_layout(dims);
+  const int R = dims->B * dims->C;
+  const int dt = dims->dtype, d = dims->d, Hq = dims->n_q_heads, Hkv = dims->n_kv_heads, dh = dims->head_dim;
+  void* X = io->x_out ? io->x_out : at(ws, L.X);
+  void* Q = io->q_out ? io->q_out : at(ws, L.Q);
+  void* Kn = io->k_new_out ? io->k_new_out : at(ws, L.Kn);
+  void* Vn = io->v_new_out ? io->v_new_out : at(ws, L.Vn);
+  void* O = io->attn_out ? io->attn_out : at(ws, L.O);
+  void* Z = io->z_out ? io->z_out : at(ws, L.Z);
+  void* scratch = at(ws, L.scratch);
+  hipError_t e;
+  if ((e = dg::launch_assemble(dt, R, d, dims->V, io->H, w->E, io->tokens_in, io->selfcond_in, X, s)) != hipSuccess)
+    return hip_fail(e, "assemble");
+  if ((e = dg::launch_gemm_qkv(dt, R, d, X, w->Wq, Hq * dh, Q, w->Wk, w->Wv, Hkv * dh, Kn, Vn, s)) != hipSuccess)
+    return hip_fail(e, "Q/K/V projections");
+  dg::AttnPlan ap = dg::attn_plan(dims->B, dims->C, dims->L, dims->cap, Hq, Hkv, dh, dt, 0);
+  if ((e = dg::launch_attn(ap, Q, io->k_cache, io->v_cache, Kn, Vn, O, nullptr, scratch, s,
+                           (hipEvent_t)io->ev_attn_begin, (hipEvent_t)io->ev_attn_end)) != hipSuccess)
+    return hip_fail(e, "attention");
+  if ((e = dg::launch_gemm_nt(dt, R, d, Hq * dh, O, w->Wo, X, Z, s)) != hipSuccess) return hip_fail(e, "output projection");
+  dg::VocabPlan vp = dg::vocab_plan(R, d, dims->V, dt);
+  if ((e = dg::launch_vocab(vp, Z, dt == DG_BF16 ? w->E_tiled : w->E, io->max_logit, io->argmax, io->conf, io->lse, io->selfcond_out,
+                            scratch, s, (hipEvent_t)io->ev_vocab_begin, (hipEvent_t)io->ev_vocab_end)) != hipSuccess)
+    return hip_fail(e, "vocab/self-conditioning");
+  if ((e = dg::launch_renoise(R, dims->C, dims->V, io->argmax, io->conf, tau, seed, t, block,
+                              io->tokens_out, io->mask, s)) != hipSuccess)
+    return hip_fail(e, "renoise");
+  return DG_OK;
+}
+
+int check_append(const dg_dims* dims, const dg_weights* w, const void* H, const int32_t* tokens_final,
+                 const void* k_cache, const void* v_cache, const void* attn_out, const void* ws,
+                 size_t ws_bytes) {
+  int st = check_dims(dims, true);
+  if (st != DG_OK) return st;
+  if (!w || !w->Wq || !w->Wk || !w->Wv || !w->E || !H || !tokens_final || !k_cache || !v_cache)
+    return fail(DG_EINVAL, "weights (Wq, Wk, Wv, E), H, tokens_final and the caches must be non-NULL");
+  if (dims->L + dims->C > dims->cap)
+    return fail(DG_EINVAL, "append needs L + C <= cap (L=%d C=%d cap=%d)", dims->L, dims->C, dims->cap);
+  if (dims->dtype == DG_BF16 && dims->d % 64)
+    return fail(DG_EUNSUPPORTED, "bf16 append needs d %% 64 == 0");
+  const void* ptrs[] = {w->Wq, w->Wk, w->Wv, w->E, H, k_cache, v_cache, attn_out};
+  if ((st = check_bf16_align(dims, ptrs, 8)) != DG_OK) return st;
+  const StepLayout L = step_layout(dims);
+  if (!ws || ws_bytes < L.total)
+    return fail(DG_EWORKSPACE, "append workspace needs %zu bytes (got %zu)", L.total, ws ? ws_bytes : 0);
+  return DG_OK;
+}
+
+int enqueue_append(const dg_dims* dims, const dg_weights* w, const void* H, const int32_t* tokens_final,
+                   void* k_cache, void* v_cache, void* attn_out, void* ws, hipStream_t s) {
+  const StepLayout L = step_layout(dims);
+  const int dt = dims->dtype, d = dims->d, Hq = dims->n_q_heads, Hkv = dims->n_kv_heads, dh = dims->head_dim;
+  const int R = dims->B * dims->C;
+  void* X = at(ws, L.X);
+  void* Q = at(ws, L.Q);
+  void* Kn = at(ws, L.Kn);
+  void* Vn = at(ws, L.Vn);
+  void* O = attn_out ? attn_out : at(ws, L.O);
+  hipError_t e;
+  if ((e = dg::launch_assemble(dt, R, d, dims->V, H, w->E, tokens_final, nullptr, X, s)) != hipSuccess)
+    return hip_fail(e, "assemble");
+  if ((e = dg::launch_gemm_qkv(dt, R, d, X, w->Wq, Hq * dh, Q, w->Wk, w->Wv, Hkv * dh, Kn, Vn, s)) != hipSuccess)
+    return hip_fail(e, "Q/K/V projections");
+  if ((e = dg::launch_cache_append(dt, dims->B, dims->C, dims->L, dims->cap, Hkv, dh, Kn, k_cache, s)) != hipSuccess)
+    return hip_fail(e, "K cache append");
+  if ((e = dg::launch_cache_append(dt, dims->B, dims->C, dims->L, dims->cap, Hkv, dh, Vn, v_cache, s)) != hipSuccess)
+    return hip_fail(e, "V cache append");
+  dg::AttnPlan ap = dg::attn_plan(dims->B, dims->C, dims->L, dims->cap, Hq, Hkv, dh, dt, 1);
+  if ((e = dg::launch_attn(ap, Q, k_cache, v_cache, Kn, Vn, O, nullptr, at(ws, L.scratch), s)) != hipSuccess)
+    return hip_fail(e, "causal attention");
+  return DG_OK;
+}
+
+// The per-step tensors of step s of block k in the block loop.
+dg_step_io block_step_io(const dg_dims* dims, const dg_block_io* io, int steps, int k, int s) {
+  const size_t R = (size_t)dims->B * dims->C, es = esize(dims->dtype);
+  const size_t slab = R * dims->d * es;
+  const size_t n = (size_t)k * steps + s;  // record index of this step
+  dg_step_io o{};
+  o.H = (const char*)io->H + (size_t)k * slab;
+  o.k_cache = io->k_cache;
+  o.v_cache = io->v_cache;
+  if (io->trace_tokens) {
+    o.tokens_in = s == 0 ? io->canvas : io->trace_tokens + (n - 1) * R;
+    o.tokens_out = io->trace_tokens + n * R;
+  } else {
+    o.tokens_in = io->canvas + (size_t)(s & 1) * R;
+    o.tokens_out = io->canvas + (size_t)((s + 1) & 1) * R;
+  }
+  if (io->trace_selfcond) {
+    o.selfcond_in = s == 0 ? nullptr : (const char*)io->trace_selfcond + (n - 1) * slab;
+    o.selfcond_out = (char*)io->trace_selfcond + n * slab;
+  } else {
+    o.selfcond_in = s == 0 ? nullptr : (const char*)io->selfcond + (size_t)(s & 1) * slab;
+    o.selfcond_out = (char*)io->selfcond + (size_t)((s + 1) & 1) * slab;
+  }
+  o.max_logit = io->max_logit;
+  o.conf = io->trace_conf ? io->trace_conf + n * R : io->conf;
+  o.argmax = s == steps - 1 ? io->tokens + (size_t)k * R : io->argmax;
+  o.mask = io->mask;
+  return o;
+}
+
+int check_block_loop(const dg_dims* dims, const dg_weights* w, const dg_block_io* io, const float* taus,
+                     int steps, int blocks, const void* ws, size_t ws_bytes) {
+  int st = check_dims(dims, true);
+  if (st != DG_OK) return st;
+  if (!io || !taus) return fail(DG_EINVAL, "io and taus must be non-NULL");
+  if (steps <= 0 || blocks <= 0) return fail(DG_EINVAL, "steps and blocks must be positive (%d, %d)", steps, blocks);
+  if ((long long)dims->L + (long long)blocks * dims->C > dims->cap)
+    return fail(DG_EINVAL, "block loop needs L + blocks*C <= cap (L=%d C=%d blocks=%d cap=%d)", dims->L,
+                dims->C, blocks, dims->cap);
+  if (!io->H || !io->k_cache || !io->v_cache || !io->tokens || !io->max_logit || !io->argmax ||
+      !io->canvas || (!io->selfcond && !io->trace_selfcond) || (!io->conf && !io->trace_conf))
+    return fail(DG_EINVAL, "H, the caches, tokens, canvas, selfcond (or trace_selfcond), max_logit, conf (or trace_conf) and argmax must be non-NULL");
+  const void* ptrs[] = {io->H, io->selfcond, io->trace_selfcond};
+  if ((st = check_bf16_align(dims, ptrs, 3)) != DG_OK) return st;
+  // every step and append of the loop, checked before anything is enqueued
+  for (int k = 0; k < blocks; ++k) {
+    dg_dims dk = *dims;
+    dk.L = dims->L + k * dims->C;
+    for (int s = 0; s < steps; s += (steps > 1 ? steps - 1 : 1)) {
+      const dg_step_io o = block_step_io(&dk, io, steps, k, s);
+      if ((st = check_step(&dk, w, &o, ws, ws_bytes)) != DG_OK) return st;
+    }
+    if ((st = check_append(&dk, w, block_step_io(&dk, io, steps, k, 0).H, io->tokens + (size_t)k * dims->B * dims->C,
+                           io->k_cache, io->v_cache, nullptr, ws, ws_bytes)) != DG_OK)
+      return st;
+  }
+  return DG_OK;
+}
+
+int enqueue_block_loop(const dg_dims* dims, const dg_weights* w, const dg_block_io* io, const float* taus,
+                       int steps, int blocks, uint64_t seed, void* ws, hipStream_t s) {
+  const int R = dims->B * dims->C;
+  int st;
+  for (int k = 0; k < blocks; ++k) {
+    dg_dims dk = *dims;
+    dk.L = dims->L + k * dims->C;
+    hipError_t e = dg::launch_renoise(R, dims->C, dims->V, nullptr, nullptr, 0.f, seed, 0, (uint32_t)k,
+                                      io->canvas, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "initial canvas");
+    for (int t = 0; t < steps; ++t) {
+      const dg_step_io o = block_step_io(&dk, io, steps, k, t);
+      if ((st = enqueue_step(&dk, w, &o, taus[t], seed, (uint32_t)t + 1, (uint32_t)k, ws, s)) != DG_OK) return st;
+    }
+    const dg_step_io o = block_step_io(&dk, io, steps, k, 0);
+    if ((st = enqueue_append(&dk, w, o.H, io->tokens + (size_t)k * R, io->k_cache, io->v_cache, nullptr, ws, s)) != DG_OK)
+      return st;
+  }
+  return DG_OK;
+}
+
 }  // namespace
+
+struct dg_graph_s {
+  hipGraphExec_t exec;
+};
 
 extern "C" {
 
@@ -223,93 +410,73 @@ int dg_attn_bidir(const dg_dims* dims, const void* q, const void* k_cache, const
 int dg_denoise_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io, float tau,
                     uint64_t seed, uint32_t t, uint32_t block, void* ws, size_t ws_bytes,
                     void* stream) {
-  int st = check_dims(dims, true);
+  int st = check_step(dims, w, io, ws, ws_bytes);
   if (st != DG_OK) return st;
-  if (!w || !io) return fail(DG_EINVAL, "weights and io must be non-NULL");
-  if (!w->Wq || !w->Wk || !w->Wv || !w->Wo || !w->E || (dims->dtype == DG_BF16 && !w->E_tiled))
-    return fail(DG_EINVAL, "every weight pointer (and E_tiled for bf16) must be non-NULL");
-  if (!io->H || !io->tokens_in || !io->tokens_out || !io->selfcond_out || !io->max_logit ||
-      !io->conf || !io->argmax || (dims->L > 0 && (!io->k_cache || !io->v_cache)))
-    return fail(DG_EINVAL, "H, tokens_in/out, selfcond_out, max_logit, conf, argmax (and the caches when L > 0) must be non-NULL");
-  const int R = dims->B * dims->C;
-  if ((st = check_vocab_shape(R, dims->d, dims->V, dims->dtype)) != DG_OK) return st;
-  if (dims->dtype == DG_BF16 && (dims->d % 128 || dims->n_q_heads * dims->head_dim % 64))
-    return fail(DG_EUNSUPPORTED, "bf16 step needs d %% 128 == 0 and n_q_heads*head_dim %% 64 == 0");
-  const void* ptrs[] = {w->Wq, w->Wk, w->Wv, w->Wo, w->E, io->H, io->k_cache, io->v_cache,
-                        io->selfcond_in, io->selfcond_out, io->x_out, io->q_out, io->k_new_out,
-                        io->v_new_out, io->attn_out, io->z_out, w->E_tiled};
-  if ((st = check_bf16_align(dims, ptrs, 17)) != DG_OK) return st;
-  const StepLayout L = step_layout(dims);
-  if (!ws || ws_bytes < L.total)
-    return fail(DG_EWORKSPACE, "step workspace needs %zu bytes (got %zu)", L.total, ws ? ws_bytes : 0);
-  if (!aligned16(ws)) return fail(DG_EINVAL, "workspace must be 16-byte aligned");
-
-  hipStream_t s = (hipStream_t)stream;
-  const int dt = dims->dtype, d = dims->d, Hq = dims->n_q_heads, Hkv = dims->n_kv_heads, dh = dims->head_dim;
-  void* X = io->x_out ? io->x_out : at(ws, L.X);
-  void* Q = io->q_out ? io->q_out : at(ws, L.Q);
-  void* Kn = io->k_new_out ? io->k_new_out : at(ws, L.Kn);
-  void* Vn = io->v_new_out ? io->v_new_out : at(ws, L.Vn);
-  void* O = io->attn_out ? io->attn_out : at(ws, L.O);
-  void* Z = io->z_out ? io->z_out : at(ws, L.Z);
-  void* scratch = at(ws, L.scratch);
-  hipError_t e;
-  if ((e = dg::launch_assemble(dt, R, d, dims->V, io->H, w->E, io->tokens_in, io->selfcond_in, X, s)) != hipSuccess)
-    return hip_fail(e, "assemble");
-  if ((e = dg::launch_gemm_qkv(dt, R, d, X, w->Wq, Hq * dh, Q, w->Wk, w->Wv, Hkv * dh, Kn, Vn, s)) != hipSuccess)
-    return hip_fail(e, "Q/K/V projections");
-  dg::AttnPlan ap = dg::attn_plan(dims->B, dims->C, dims->L, dims->cap, Hq, Hkv, dh, dt, 0);
-  if ((e = dg::launch_attn(ap, Q, io->k_cache, io->v_cache, Kn, Vn, O, nullptr, scratch, s,
-                           (hipEvent_t)io->ev_attn_begin, (hipEvent_t)io->ev_attn_end)) != hipSuccess)
-    return hip_fail(e, "attention");
-  if ((e = dg::launch_gemm_nt(dt, R, d, Hq * dh, O, w->Wo, X, Z, s)) != hipSuccess) return hip_fail(e, "output projection");
-  dg::VocabPlan vp = dg::vocab_plan(R, d, dims->V, dt);
-  if ((e = dg::launch_vocab(vp, Z, dt == DG_BF16 ? w->E_tiled : w->E, io->max_logit, io->argmax, io->conf, io->lse, io->selfcond_out,
-                            scratch, s, (hipEvent_t)io->ev_vocab_begin, (hipEvent_t)io->ev_vocab_end)) != hipSuccess)
-    return hip_fail(e, "vocab/self-conditioning");
-  if ((e = dg::launch_renoise(R, dims->C, dims->V, io->argmax, io->conf, tau, seed, t, block,
-                              io->tokens_out, io->mask, s)) != hipSuccess)
-    return hip_fail(e, "renoise");
-  return DG_OK;
+  return enqueue_step(dims, w, io, tau, seed, t, block, ws, (hipStream_t)stream);
 }
 
 int dg_prefill_append(const dg_dims* dims, const dg_weights* w, const void* H,
                       const int32_t* tokens_final, void* k_cache, void* v_cache, void* attn_out,
                       void* ws, size_t ws_bytes, void* stream) {
-  int st = check_dims(dims, true);
+  int st = check_append(dims, w, H, tokens_final, k_cache, v_cache, attn_out, ws, ws_bytes);
   if (st != DG_OK) return st;
-  if (!w || !w->Wq || !w->Wk || !w->Wv || !w->E || !H || !tokens_final || !k_cache || !v_cache)
-    return fail(DG_EINVAL, "weights (Wq, Wk, Wv, E), H, tokens_final and the caches must be non-NULL");
-  if (dims->L + dims->C > dims->cap)
-    return fail(DG_EINVAL, "append needs L + C <= cap (L=%d C=%d cap=%d)", dims->L, dims->C, dims->cap);
-  if (dims->dtype == DG_BF16 && dims->d % 64)
-    return fail(DG_EUNSUPPORTED, "bf16 append needs d %% 64 == 0");
-  const void* ptrs[] = {w->Wq, w->Wk, w->Wv, w->E, H, k_cache, v_cache, attn_out};
-  if ((st = check_bf16_align(dims, ptrs, 8)) != DG_OK) return st;
-  const StepLayout L = step_layout(dims);
-  if (!ws || ws_bytes < L.total)
-    return fail(DG_EWORKSPACE, "append workspace needs %zu bytes (got %zu)", L.total, ws ? ws_bytes : 0);
+  return enqueue_append(dims, w, H, tokens_final, k_cache, v_cache, attn_out, ws, (hipStream_t)stream);
+}
+
+int dg_block_loop(const dg_dims* dims, const dg_weights* w, const dg_block_io* io, const float* taus,
+                  int32_t steps, int32_t blocks, uint64_t seed, void* ws, size_t ws_bytes,
+                  void* stream) {
+  int st = check_block_loop(dims, w, io, taus, steps, blocks, ws, ws_bytes);
+  if (st != DG_OK) return st;
+  return enqueue_block_loop(dims, w, io, taus, steps, blocks, seed, ws, (hipStream_t)stream);
+}
+
+int dg_graph_capture_block_loop(const dg_dims* dims, const dg_weights* w, const dg_block_io* io,
+                                const float* taus, int32_t steps, int32_t blocks, uint64_t seed,
+                                void* ws, size_t ws_bytes, void* stream, dg_graph* graph) {
+  if (!graph) return fail(DG_EINVAL, "graph must be non-NULL");
+  *graph = nullptr;
+  if (!stream) return fail(DG_EINVAL, "graph capture needs a created stream, not the NULL stream");
+  int st = check_block_loop(dims, w, io, taus, steps, blocks, ws, ws_bytes);
+  if (st != DG_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  const int dt = dims->dtype, d = dims->d, Hq = dims->n_q_heads, Hkv = dims->n_kv_heads, dh = dims->head_dim;
-  const int R = dims->B * dims->C;
-  void* X = at(ws, L.X);
-  void* Q = at(ws, L.Q);
-  void* Kn = at(ws, L.Kn);
-  void* Vn = at(ws, L.Vn);
-  void* O = attn_out ? attn_out : at(ws, L.O);
-  hipError_t e;
-  if ((e = dg::launch_assemble(dt, R, d, dims->V, H, w->E, tokens_final, nullptr, X, s)) != hipSuccess)
-    return hip_fail(e, "assemble");
-  if ((e = dg::launch_gemm_qkv(dt, R, d, X, w->Wq, Hq * dh, Q, w->Wk, w->Wv, Hkv * dh, Kn, Vn, s)) != hipSuccess)
-    return hip_fail(e, "Q/K/V projections");
-  if ((e = dg::launch_cache_append(dt, dims->B, dims->C, dims->L, dims->cap, Hkv, dh, Kn, k_cache, s)) != hipSuccess)
-    return hip_fail(e, "K cache append");
-  if ((e = dg::launch_cache_append(dt, dims->B, dims->C, dims->L, dims->cap, Hkv, dh, Vn, v_cache, s)) != hipSuccess)
-    return hip_fail(e, "V cache append");
-  dg::AttnPlan ap = dg::attn_plan(dims->B, dims->C, dims->L, dims->cap, Hq, Hkv, dh, dt, 1);
-  if ((e = dg::launch_attn(ap, Q, k_cache, v_cache, Kn, Vn, O, nullptr, at(ws, L.scratch), s)) != hipSuccess)
-    return hip_fail(e, "causal attention");
+  hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+  st = enqueue_block_loop(dims, w, io, taus, steps, blocks, seed, ws, s);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(s, &g);
+  if (st != DG_OK) {
+    if (g) hipGraphDestroy(g);
+    return st;
+  }
+  if (e != hipSuccess) {
+    if (g) hipGraphDestroy(g);
+    return hip_fail(e, "hipStreamEndCapture");
+  }
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiateWithFlags(&x, g, 0);
+  hipGraphDestroy(g);
+  if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
+  dg_graph out = new (std::nothrow) dg_graph_s;
+  if (!out) {
+    hipGraphExecDestroy(x);
+    return fail(DG_EINVAL, "out of host memory");
+  }
+  out->exec = x;
+  *graph = out;
   return DG_OK;
+}
+
+int dg_graph_launch(dg_graph graph, void* stream) {
+  if (!graph || !graph->exec) return fail(DG_EINVAL, "graph is NULL");
+  hipError_t e = hipGraphLaunch(graph->exec, (hipStream_t)stream);
+  return e == hipSuccess ? DG_OK : hip_fail(e, "hipGraphLaunch");
+}
+
+void dg_graph_destroy(dg_graph graph) {
+  if (!graph) return;
+  if (graph->exec) hipGraphExecDestroy(graph->exec);
+  delete graph;
 }
 
 }  // extern "C"
