@@ -127,6 +127,53 @@ def attention_hbm_shape(stream, reps=20):
             "mfma_frac": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
 
 
+def block_loop_graph(stream, replays=2):
+    """The block-diffusion workload (8 canvases of 256 tokens over their own
+    4096-row caches, 4 blocks of 32 steps with tau annealed 0.5 -> 0.95, a
+    causal append after each block) captured into one HIP graph by
+    dg_graph_capture_block_loop; times whole-sequence replays with HIP events
+    on the replay stream."""
+    import torch
+    import uniform_state_discrete_amd as dg
+    from synth import config_by_name, gen_problem, tau_schedule
+    c = config_by_name("blocks4_canvas8x256_L4096_d2048_V262144")
+    p = gen_problem(c)
+    W = {k: dg.to_device(v) for k, v in p.W.items()}
+    W["E"] = dg.to_device(p.E)
+    W["E_tiled"] = dg.tiled_embedding(W["E"])
+    Kc, Vc = dg.to_device(p.Kc), dg.to_device(p.Vc)
+    H = torch.stack([dg.to_device(h) for h in p.H]).contiguous()
+    del p
+    dims = dg.make_dims(c.B, c.C, c.L, c.cap, c.d, c.Hq, c.Hkv, c.dh, c.V, dg.DG_BF16)
+    ws = dg.workspace(dg.dg_workspace_bytes(dims))
+    R = c.R
+    i32 = dict(dtype=torch.int32, device="cuda")
+    io = dict(H=H, k_cache=Kc, v_cache=Vc, tokens=torch.zeros((c.blocks, c.B, c.C), **i32),
+              canvas=torch.zeros((2, c.B, c.C), **i32),
+              selfcond=torch.zeros((2, c.B, c.C, c.d), dtype=torch.bfloat16, device="cuda"),
+              max_logit=torch.empty(R, device="cuda"), conf=torch.empty(R, device="cuda"),
+              argmax=torch.empty(R, **i32), mask=torch.empty(R, dtype=torch.uint8, device="cuda"))
+    taus = tau_schedule(c)
+    g = dg.dg_graph_capture_block_loop(dims, W, io, taus, c.steps, c.blocks, c.seed, ws, stream)
+    g.launch(stream)                        # warm-up replay
+    stream.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        g.launch(stream)
+    e1.record(stream)
+    stream.synchronize()
+    ms = e0.elapsed_time(e1) / replays
+    g.close()
+    n_steps = c.steps * c.blocks
+    alg = algorithmic(c)
+    return {"workload": c.name, "graph_replays": replays, "ms_per_sequence": round(ms, 3),
+            "sequence": f"{c.blocks} blocks x ({c.steps} denoise steps + causal append) over {c.B} canvases",
+            "steps_per_s": round(n_steps / (ms * 1e-3), 2),
+            "canvas_tokens_per_s": round(n_steps * R / (ms * 1e-3), 1),
+            "step_mfma_frac": round(alg["flops"] * n_steps / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def copy_calibration(mib):
     """A plain device-to-device copy of known size, for scaling HBM counters."""
     import torch
@@ -147,6 +194,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn-hbm", action="store_true", help="skip the HBM-bound attention shape")
+    ap.add_argument("--no-block-loop", action="store_true", help="skip the block-diffusion graph replay")
     ap.add_argument("--copy-mib", type=int, default=0, help="only run a plain copy of this size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -262,6 +310,8 @@ def main():
     }
     if not args.no_attn_hbm:
         out["attention_hbm_shape"] = attention_hbm_shape(stream)
+    if not args.no_block_loop:
+        out["block_loop_graph"] = block_loop_graph(torch.cuda.Stream())
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, cfg)
     print(json.dumps(out), flush=True)
