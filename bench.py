@@ -174,6 +174,61 @@ def block_loop_graph(stream, replays=2):
             "step_mfma_frac": round(alg["flops"] * n_steps / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def crossover_sweep(stream, reps=10):
+    """Time of the fused vocabulary head (logits, softmax statistics, P.E over
+    the 262144 x 2048 bf16 table) and of canvas attention (over an 8192-row
+    cache, 16/8 heads of 128) as the number of canvas rows M grows: one user's
+    canvas rows against many users' rows batched together.  While the kernels
+    are bound by streaming E or the cache their time stays flat; past the
+    ridge it grows with M."""
+    import torch
+    import uniform_state_discrete_amd as dg
+    d, V = 2048, 262144
+    g = torch.Generator(device="cuda").manual_seed(4004)
+    E = (torch.randn(V, d, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    Et = dg.tiled_embedding(E)
+    del E
+    L, Hq, Hkv, dh = 8192, 16, 8, 128
+    Kc = torch.randn(1, Hkv, L, dh, generator=g, device="cuda").to(torch.bfloat16) * (d ** -0.5)
+    Vc = torch.randn(1, Hkv, L, dh, generator=g, device="cuda").to(torch.bfloat16) * (d ** -0.5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    out = []
+    for M in (1, 8, 32, 64, 128, 156, 256, 512, 1024, 2048):
+        Z = (torch.randn(M, d, generator=g, device="cuda") * 0.3).to(torch.bfloat16)
+        st = [torch.empty(M, device="cuda") for _ in range(3)]
+        am = torch.empty(M, dtype=torch.int32, device="cuda")
+        S = torch.empty(M, d, dtype=torch.bfloat16, device="cuda")
+        ws = dg.workspace(dg.dg_vocab_workspace_bytes(M, d, V, dg.DG_BF16))
+        vu = timed(lambda: dg.dg_vocab_selfcond(M, d, V, Z, Et, st[0], am, st[1], st[2], S, ws, stream))
+        q = torch.randn(1, M, Hq, dh, generator=g, device="cuda").to(torch.bfloat16)
+        kn = torch.randn(1, M, Hkv, dh, generator=g, device="cuda").to(torch.bfloat16) * (d ** -0.5)
+        vn = torch.randn(1, M, Hkv, dh, generator=g, device="cuda").to(torch.bfloat16) * (d ** -0.5)
+        o = torch.empty_like(q)
+        dims = dg.make_dims(1, M, L, L, d, Hq, Hkv, dh, 0, dg.DG_BF16)
+        wa = dg.workspace(dg.dg_attn_workspace_bytes(dims))
+        au = timed(lambda: dg.dg_attn_bidir(dims, q, Kc, Vc, kn, vn, o, None, 0, wa, stream))
+        vfl = 4.0 * M * V * d
+        afl = 4.0 * M * (L + M) * Hq * dh
+        out.append({"rows": M, "vocab_us": round(vu, 2), "vocab_TFLOPs": round(vfl / vu / 1e6, 1),
+                    "vocab_E_GBs": round(V * d * 2 / vu / 1e3, 1),
+                    "attn_us": round(au, 2), "attn_TFLOPs": round(afl / au / 1e6, 1),
+                    "attn_cache_GBs": round(2 * L * Hkv * dh * 2 / au / 1e3, 1)})
+        print(json.dumps(out[-1]), flush=True)
+    return out
+
+
 def copy_calibration(mib):
     """A plain device-to-device copy of known size, for scaling HBM counters."""
     import torch
@@ -195,6 +250,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn-hbm", action="store_true", help="skip the HBM-bound attention shape")
     ap.add_argument("--no-block-loop", action="store_true", help="skip the block-diffusion graph replay")
+    ap.add_argument("--sweep-rows", action="store_true",
+                    help="only run the rows sweep of the vocabulary head and attention (one JSON line per size)")
     ap.add_argument("--copy-mib", type=int, default=0, help="only run a plain copy of this size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -203,6 +260,11 @@ def main():
         sys.exit(2)
     if args.copy_mib:
         copy_calibration(args.copy_mib)
+        return
+    if args.sweep_rows:
+        import torch
+        torch.cuda.set_device(0)
+        crossover_sweep(torch.cuda.current_stream())
         return
 
     import numpy as np
