@@ -183,7 +183,62 @@ def init_canvas(seed, block, B, C, V):
     return draw_tokens(seed, 0, block, B, C, V)
 
 
+# -- masked diffusion --------------------------------------------------------------
+
+def unmask(a, c, tau, x, mask_id):
+    """"Diffusione mascherata": noise is an explicit [MASK] token; in the
+    reverse process the model predicts the token behind each mask and the
+    prediction replaces the mask where its confidence meets the threshold.
+    A replaced token is locked: later steps never change it.  Readings: the
+    confidence is c (max probability) and "meets" is c >= tau (tau taken as a
+    float32, the complement of the uniform-state "below"); the committed
+    token is the argmax a; a prediction equal to the mask id commits nothing
+    (the position stays masked); [MASK] is a caller-chosen vocabulary id.
+    a, c, x: [B*C] -> new tokens [B*C] int64, newly committed [B*C] uint8."""
+    tau32 = float(np.float32(tau))
+    x = np.asarray(x, np.int64).reshape(-1)
+    a = np.asarray(a, np.int64).reshape(-1)
+    commit = (x == mask_id) & (np.asarray(c, np.float64).reshape(-1) >= tau32) & (a != mask_id)
+    return np.where(commit, a, x), commit.astype(np.uint8)
+
+
+def init_masked(B, C, mask_id):
+    """A masked-diffusion canvas starts fully masked (all noise)."""
+    return np.full((B, C), mask_id, np.int64)
+
+
 # -- the step -------------------------------------------------------------------
+
+def forward(H, E, W, Kc, Vc, L, x, S_prev, dtype):
+    """Steps 1-5 of a denoise step, shared by both samplers: the model reads
+    the canvas and returns every intermediate, the prediction a, its
+    confidence c and the self-conditioning vector S."""
+    B, C, d = H.shape
+    dh = Kc.shape[3]
+    Hq = W["Wq"].shape[0] // dh
+    Hkv = W["Wk"].shape[0] // dh
+    X = assemble(H, E, x, S_prev, dtype)
+    Xf = X.reshape(B * C, d)
+    Q = linear(Xf, W["Wq"], dtype).reshape(B, C, Hq, dh)
+    Kn = linear(Xf, W["Wk"], dtype).reshape(B, C, Hkv, dh)
+    Vn = linear(Xf, W["Wv"], dtype).reshape(B, C, Hkv, dh)
+    O, lse_att = attention(Q, Kc, Vc, Kn, Vn, L, causal=False, dtype=dtype)
+    Z = round_store(Xf + O.reshape(B * C, Hq * dh) @ W["Wo"].T, dtype)
+    m, a, lse, c, S = vocab_selfcond(Z, E, dtype)
+    return dict(X=X, Q=Q, Kn=Kn, Vn=Vn, O=O, lse_att=lse_att, Z=Z.reshape(B, C, d),
+                m=m, a=a, lse=lse, c=c, S=S.reshape(B, C, d))
+
+
+def denoise_step_masked(H, E, W, Kc, Vc, L, x, S_prev, tau, mask_id, dtype):
+    """One step of the masked-diffusion sampler: the same model pass as
+    denoise_step, then unmask-and-lock instead of the uniform renoise.
+    Returns the intermediates plus x_new and `commit` (newly unmasked)."""
+    B, C, _ = H.shape
+    r = forward(H, E, W, Kc, Vc, L, x, S_prev, dtype)
+    x_new, commit = unmask(r["a"], r["c"], tau, x, mask_id)
+    r.update(x_new=x_new.reshape(B, C), commit=commit.reshape(B, C))
+    return r
+
 
 def denoise_step(H, E, W, Kc, Vc, L, x, S_prev, tau, seed, t, block, dtype):
     """One denoise step over all B canvases.  W = dict(Wq, Wk, Wv, Wo).
@@ -197,23 +252,12 @@ def denoise_step(H, E, W, Kc, Vc, L, x, S_prev, tau, seed, t, block, dtype):
     The cache is only read (denoise never writes it; only prefill does,
     "Architettura...").  Returns a dict of every intermediate.
     """
-    B, C, d = H.shape
-    dh = Kc.shape[3]
-    Hq = W["Wq"].shape[0] // dh
-    Hkv = W["Wk"].shape[0] // dh
+    B, C, _ = H.shape
     V = E.shape[0]
-    X = assemble(H, E, x, S_prev, dtype)
-    Xf = X.reshape(B * C, d)
-    Q = linear(Xf, W["Wq"], dtype).reshape(B, C, Hq, dh)
-    Kn = linear(Xf, W["Wk"], dtype).reshape(B, C, Hkv, dh)
-    Vn = linear(Xf, W["Wv"], dtype).reshape(B, C, Hkv, dh)
-    O, lse_att = attention(Q, Kc, Vc, Kn, Vn, L, causal=False, dtype=dtype)
-    Z = round_store(Xf + O.reshape(B * C, Hq * dh) @ W["Wo"].T, dtype)
-    m, a, lse, c, S = vocab_selfcond(Z, E, dtype)
-    x_new, mask = renoise(a, c, tau, seed, t, block, B, C, V)
-    return dict(X=X, Q=Q, Kn=Kn, Vn=Vn, O=O, lse_att=lse_att, Z=Z.reshape(B, C, d),
-                m=m, a=a, lse=lse, c=c, S=S.reshape(B, C, d),
-                x_new=x_new.reshape(B, C), mask=mask.reshape(B, C))
+    r = forward(H, E, W, Kc, Vc, L, x, S_prev, dtype)
+    x_new, mask = renoise(r["a"], r["c"], tau, seed, t, block, B, C, V)
+    r.update(x_new=x_new.reshape(B, C), mask=mask.reshape(B, C))
+    return r
 
 
 def prefill_append(H, E, W, Kc, Vc, L, x_final, dtype):
