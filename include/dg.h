@@ -177,6 +177,27 @@ int dg_renoise(int32_t rows, int32_t canvas, int32_t V, const int32_t *argmax, c
 int dg_init_canvas(int32_t rows, int32_t canvas, int32_t V, uint64_t seed, uint32_t block,
                    int32_t *tokens_out, void *stream);
 
+/* Masked diffusion ("Diffusione mascherata"), the sampler the pages contrast
+ * with uniform-state diffusion: noise is an explicit [MASK] token, here the
+ * caller-chosen vocabulary id mask_id.  Row r becomes
+ *   tokens_in[r] == mask_id && conf[r] >= tau && argmax[r] != mask_id
+ *       ? argmax[r] : tokens_in[r]
+ * so a committed token is locked (never changed again) and a prediction of
+ * the mask id itself commits nothing.  commit_out[r] = 1 where this call
+ * unmasked the row (may be NULL).  tokens_out may equal tokens_in. */
+int dg_unmask(int32_t rows, const int32_t *argmax, const float *conf, float tau, int32_t mask_id,
+              const int32_t *tokens_in, int32_t *tokens_out, uint8_t *commit_out, void *stream);
+
+/* A fully masked canvas: every row of tokens_out[rows] set to mask_id. */
+int dg_init_masked(int32_t rows, int32_t mask_id, int32_t *tokens_out, void *stream);
+
+/* One step of the masked sampler: the model pass of dg_denoise_step (same
+ * dims, weights, io and workspace), then dg_unmask instead of the
+ * uniform-state renoise.  io->mask receives the commit flags.  mask_id must
+ * lie in [0, V). */
+int dg_denoise_step_masked(const dg_dims *dims, const dg_weights *w, const dg_step_io *io,
+                           float tau, int32_t mask_id, void *ws, size_t ws_bytes, void *stream);
+
 /* Incremental prefill of a finished block ("Architettura...", causal
  * prefill; "Campionamento multi-canvas (diffusione a blocchi)"):
  * X = H + E[tokens_final] (no self-conditioning), canvas keys/values

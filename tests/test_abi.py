@@ -173,3 +173,20 @@ def test_block_loop_and_graph_argument_checks(L):
                                            FAKE, 1 << 40, FAKE, None) == L.DG_EINVAL
     assert lib.dg_graph_launch(None, None) == L.DG_EINVAL
     lib.dg_graph_destroy(None)
+
+
+def test_masked_sampler_argument_checks(L):
+    lib = L.lib()
+    assert lib.dg_unmask(0, FAKE, FAKE, 0.5, 3, FAKE, FAKE, None, None) == L.DG_EINVAL
+    assert lib.dg_unmask(16, FAKE, FAKE, 0.5, -1, FAKE, FAKE, None, None) == L.DG_EINVAL
+    assert lib.dg_unmask(16, None, FAKE, 0.5, 3, FAKE, FAKE, None, None) == L.DG_EINVAL
+    assert lib.dg_unmask(16, FAKE, FAKE, 0.5, 3, None, FAKE, None, None) == L.DG_EINVAL
+    assert lib.dg_init_masked(16, 3, None, None) == L.DG_EINVAL
+    assert lib.dg_init_masked(0, 3, FAKE, None) == L.DG_EINVAL
+    w = L.Weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    io = L.StepIO(*[FAKE if k in ("H", "k_cache", "v_cache", "tokens_in", "tokens_out", "selfcond_out",
+                                  "max_logit", "conf", "argmax") else None for k in L.STEP_IO_FIELDS])
+    for mid in (-1, 32768):   # outside [0, V)
+        st = lib.dg_denoise_step_masked(ctypes.byref(dims()), ctypes.byref(w), ctypes.byref(io), 0.9, mid,
+                                        FAKE, 1 << 40, None)
+        assert st == L.DG_EINVAL and b"mask_id" in lib.dg_last_error()

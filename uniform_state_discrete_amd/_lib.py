@@ -92,6 +92,10 @@ def lib():
                                                            ctypes.POINTER(ctypes.c_void_p)]),
             "dg_graph_launch": (ctypes.c_int, [vp, vp]),
             "dg_graph_destroy": (None, [vp]),
+            "dg_unmask": (ctypes.c_int, [i32, vp, vp, f32, i32, vp, vp, vp, vp]),
+            "dg_init_masked": (ctypes.c_int, [i32, i32, vp, vp]),
+            "dg_denoise_step_masked": (ctypes.c_int, [pd, ctypes.POINTER(Weights), ctypes.POINTER(StepIO),
+                                                      f32, i32, vp, sz, vp]),
             "dg_status_str": (ctypes.c_char_p, [ctypes.c_int]),
             "dg_last_error": (ctypes.c_char_p, []),
         }
@@ -318,3 +322,31 @@ def dg_graph_capture_block_loop(dims, weights, io, taus, steps, blocks, seed, ws
                                            ctypes.byref(h))
     _check(st, "dg_graph_capture_block_loop")
     return Graph(h.value, (dict(weights), dict(io), ws))
+
+
+def dg_unmask(rows, argmax, conf, tau, mask_id, tokens_in, tokens_out, commit_out, stream=None):
+    st = lib().dg_unmask(int(rows), ptr(argmax, torch.int32), ptr(conf, torch.float32), float(tau), int(mask_id),
+                         ptr(tokens_in, torch.int32), ptr(tokens_out, torch.int32), ptr(commit_out, torch.uint8),
+                         stream_handle(stream))
+    _check(st, "dg_unmask")
+
+
+def dg_init_masked(rows, mask_id, tokens_out, stream=None):
+    st = lib().dg_init_masked(int(rows), int(mask_id), ptr(tokens_out, torch.int32), stream_handle(stream))
+    _check(st, "dg_init_masked")
+
+
+def dg_denoise_step_masked(dims, weights, io, tau, mask_id, ws, stream=None):
+    """As dg_denoise_step, with the masked sampler; io["mask"] receives the
+    commit flags."""
+    _check_float_dtype(dims, [(k, weights.get(k)) for k in WEIGHT_FIELDS] +
+                       [(k, io.get(k)) for k in _FLOAT_IO])
+    for k in ("tokens_in", "tokens_out", "argmax"):
+        if io.get(k) is not None and io[k].dtype != torch.int32:
+            raise TypeError(f"{k}: expected torch.int32")
+    w = Weights(*(ptr(weights.get(k)) for k in WEIGHT_FIELDS))
+    s = StepIO(*((event_handle(io.get(k)) if k in EVENT_FIELDS else ptr(io.get(k))) for k in STEP_IO_FIELDS))
+    st = lib().dg_denoise_step_masked(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(s), float(tau),
+                                      int(mask_id), ptr(ws), ws.numel() if ws is not None else 0,
+                                      stream_handle(stream))
+    _check(st, "dg_denoise_step_masked")

@@ -143,8 +143,11 @@ int check_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io, c
   return DG_OK;
 }
 
+// The model pass of a step, then the sampler: uniform-state renoise
+// (mask_id < 0) or the masked sampler's unmask-and-lock (mask_id >= 0).
 int enqueue_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io, float tau,
-                 uint64_t seed, uint32_t t, uint32_t block, void* ws, hipStream_t s) {
+                 uint64_t seed, uint32_t t, uint32_t block, void* ws, hipStream_t s,
+                 int32_t mask_id = -1) {
   const StepLayout L = step_layout(dims);
   const int R = dims->B * dims->C;
   const int dt = dims->dtype, d = dims->d, Hq = dims->n_q_heads, Hkv = dims->n_kv_heads, dh = dims->head_dim;
@@ -169,6 +172,12 @@ int enqueue_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io,
   if ((e = dg::launch_vocab(vp, Z, dt == DG_BF16 ? w->E_tiled : w->E, io->max_logit, io->argmax, io->conf, io->lse, io->selfcond_out,
                             scratch, s, (hipEvent_t)io->ev_vocab_begin, (hipEvent_t)io->ev_vocab_end)) != hipSuccess)
     return hip_fail(e, "vocab/self-conditioning");
+  if (mask_id >= 0) {
+    if ((e = dg::launch_unmask(R, io->argmax, io->conf, tau, mask_id, io->tokens_in, io->tokens_out, io->mask,
+                               s)) != hipSuccess)
+      return hip_fail(e, "unmask");
+    return DG_OK;
+  }
   if ((e = dg::launch_renoise(R, dims->C, dims->V, io->argmax, io->conf, tau, seed, t, block,
                               io->tokens_out, io->mask, s)) != hipSuccess)
     return hip_fail(e, "renoise");
@@ -413,6 +422,32 @@ int dg_denoise_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* 
   int st = check_step(dims, w, io, ws, ws_bytes);
   if (st != DG_OK) return st;
   return enqueue_step(dims, w, io, tau, seed, t, block, ws, (hipStream_t)stream);
+}
+
+int dg_denoise_step_masked(const dg_dims* dims, const dg_weights* w, const dg_step_io* io, float tau,
+                           int32_t mask_id, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_step(dims, w, io, ws, ws_bytes);
+  if (st != DG_OK) return st;
+  if (mask_id < 0 || mask_id >= dims->V) return fail(DG_EINVAL, "mask_id must lie in [0, V) (got %d, V=%d)", mask_id, dims->V);
+  return enqueue_step(dims, w, io, tau, 0, 0, 0, ws, (hipStream_t)stream, mask_id);
+}
+
+int dg_unmask(int32_t rows, const int32_t* argmax, const float* conf, float tau, int32_t mask_id,
+              const int32_t* tokens_in, int32_t* tokens_out, uint8_t* commit_out, void* stream) {
+  if (rows <= 0 || mask_id < 0) return fail(DG_EINVAL, "rows must be positive and mask_id non-negative (%d, %d)", rows, mask_id);
+  if (!argmax || !conf || !tokens_in || !tokens_out)
+    return fail(DG_EINVAL, "argmax, conf, tokens_in and tokens_out must be non-NULL");
+  hipError_t e = dg::launch_unmask(rows, argmax, conf, tau, mask_id, tokens_in, tokens_out, commit_out,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? DG_OK : hip_fail(e, "dg_unmask");
+}
+
+int dg_init_masked(int32_t rows, int32_t mask_id, int32_t* tokens_out, void* stream) {
+  if (rows <= 0 || mask_id < 0) return fail(DG_EINVAL, "rows must be positive and mask_id non-negative (%d, %d)", rows, mask_id);
+  if (!tokens_out) return fail(DG_EINVAL, "tokens_out must be non-NULL");
+  hipError_t e = dg::launch_unmask(rows, nullptr, nullptr, 0.f, mask_id, nullptr, tokens_out, nullptr,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? DG_OK : hip_fail(e, "dg_init_masked");
 }
 
 int dg_prefill_append(const dg_dims* dims, const dg_weights* w, const void* H,

@@ -107,6 +107,9 @@ hipError_t launch_assemble(int dtype, int R, int d, int V, const void* H, const 
 hipError_t launch_renoise(int rows, int canvas, int V, const int32_t* argmax, const float* conf,
                           float tau, uint64_t seed, uint32_t t, uint32_t block, int32_t* out,
                           uint8_t* mask, hipStream_t s);
+// Masked diffusion: unmask-and-lock (in == NULL: a fully masked canvas).
+hipError_t launch_unmask(int rows, const int32_t* argmax, const float* conf, float tau, int32_t mask_id,
+                         const int32_t* in, int32_t* out, uint8_t* commit, hipStream_t s);
 // Scatter canvas rows kn[B][C][Hkv][dh] into cache[B][Hkv][cap][dh] at rows [L, L+C).
 hipError_t launch_cache_append(int dtype, int B, int C, int L, int cap, int Hkv, int dh,
                                const void* kn, void* cache, hipStream_t s);

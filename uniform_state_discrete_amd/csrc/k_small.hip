@@ -117,6 +117,38 @@ hipError_t launch_renoise(int rows, int canvas, int V, const int32_t* argmax, co
   return hipGetLastError();
 }
 
+// Masked diffusion (explainer, "Diffusione mascherata"): a position holding
+// the mask id takes the model's prediction when the confidence meets tau and
+// the prediction is not the mask id itself; every other position keeps its
+// token, so a committed token is locked.  in == NULL writes a fully masked
+// canvas.  commit (may be NULL) flags the positions unmasked by this call.
+__global__ void k_unmask(int rows, const int32_t* __restrict__ argmax, const float* __restrict__ conf,
+                         float tau, int32_t mask_id, const int32_t* in, int32_t* out,
+                         uint8_t* __restrict__ commit) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  int tok = mask_id;
+  bool take = false;
+  if (in) {
+    tok = in[r];
+    if (tok == mask_id) {
+      const int a = argmax[r];
+      take = (conf[r] >= tau) && (a != mask_id);
+      tok = take ? a : tok;
+    }
+  }
+  out[r] = tok;
+  if (commit) commit[r] = take ? 1 : 0;
+}
+
+hipError_t launch_unmask(int rows, const int32_t* argmax, const float* conf, float tau, int32_t mask_id,
+                         const int32_t* in, int32_t* out, uint8_t* commit, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_unmask, dim3((rows + 255) / 256), dim3(256), 0, s, rows, argmax, conf, tau, mask_id,
+                     in, out, commit);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Cache append: canvas rows kn[b][i][g][:] -> cache[b][g][L + i][:].
 // One 16-byte (bf16) or 4-byte (fp32) element group per lane.
