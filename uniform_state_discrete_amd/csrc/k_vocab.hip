@@ -653,14 +653,26 @@ __device__ __forceinline__ u32x4 pair_load(const char* base, uint32_t off) {
   return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
 }
 
+// 16-byte unit, inside a 1 KiB LDS block of 16 ids x 32 columns, holding id i,
+// columns 8gp..8gp+7 (gp < 4) as one lane of the tiled table stores them:
+// 16 gp + (i ^ 4 gp).  Each 16-lane group of the staging stores (lanes
+// 16g + r, one 16-byte store each) fills 16 distinct units of 4 banks, and
+// each 32-lane group of the transposing reads (ids 4k + 0..3 or 8 + 4k +
+// 0..3, all 8 column groups, 8 bytes each) covers the 64 banks once.  A
+// padded row layout written with two 8-byte stores per lane conflicted on
+// the stores.
+__device__ __forceinline__ int pair_lds_unit(int i, int gp) { return 16 * gp + (i ^ (4 * gp)); }
+
 template <int SLICE>
 __global__ void __launch_bounds__(256, 1)
     k_vocab_pair(const u16* __restrict__ Z, const u16* __restrict__ E, int R, int d, int V, int nrb,
                  int split_len, float* __restrict__ pS, f32x4* __restrict__ pstat,
                  uint32_t* __restrict__ xhdr, uint64_t* __restrict__ xrec) {
-  constexpr int NCH = SLICE / 32, EP = SLICE + 8;
+  constexpr int NCH = SLICE / 32;
   static_assert(NCH == 8, "the stage schedule assumes 8 chunks per tile");
-  __shared__ __attribute__((aligned(16))) u16 Et[4][4][16][EP];     // [tile & 3][wave]
+  // [tile & 3][wave][chunk]: 1 KiB per chunk of 16 ids x 32 columns in 16-byte
+  // units (pair_lds_unit), no padding
+  __shared__ __attribute__((aligned(16))) u16 Et[4][4][NCH][512];
   __shared__ __attribute__((aligned(16))) f32x4 xch[4][4][64];      // [writer wave][row group][rotated lane]
   __shared__ __attribute__((aligned(16))) u32x4 Pbuf[2][64];        // P of row m, ids 8k..8k+7
   __shared__ float Sbuf[64];                                        // per-row fold factor
@@ -695,7 +707,7 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       DG_LDS u16* ep = (DG_LDS u16*)&Et[b][w][0][0];
-      for (int e = l * 8; e < 16 * EP; e += 64 * 8) *(DG_LDS u32x4*)(ep + e) = z4;
+      for (int e = l * 8; e < NCH * 512; e += 64 * 8) *(DG_LDS u32x4*)(ep + e) = z4;
     }
   }
   __syncthreads();
@@ -722,11 +734,19 @@ __global__ void __launch_bounds__(256, 1)
   const int nt4 = nt & ~3;
   auto phys = [&](int s) { return s < nt4 ? (s & ~3) | ((s + rb) & 3) : s; };
 
-  const int wr_a = prow16t(r) * EP + 8 * g + ((g & 1) ? 4 : 0), wr_b = wr_a ^ 4;
+  // this lane's 16 bytes (id r, columns 8g..8g+7 of a chunk, in the tiled
+  // table's order) go to one unit; the transposing reads take ids
+  // 8 h2 + 4k + p/4, column group cg = 4 b4 + p % 4 (p = l % 16, b4 = bit 4
+  // of l) from the 8-byte half of unit (id, cg / 2) that holds it (the odd
+  // pairs store their upper half first).  Ids 4 apart flip bit 2 of the
+  // unit's low part: the second read offset is the first with bit 5 flipped.
+  const int wr = 8 * pair_lds_unit(r, g);
   int tr_off[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k)
-    tr_off[k] = prow16t(8 * h2 + 4 * k + ((l & 15) >> 2)) * EP + 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  {
+    const int p = l & 15, cg = 4 * ((l >> 4) & 1) + (p & 3), gp = cg >> 1;
+    tr_off[0] = 8 * pair_lds_unit(8 * h2 + (p >> 2), gp) + 4 * ((cg & 1) ^ (gp & 1));
+    tr_off[1] = tr_off[0] ^ 32;
+  }
 
   const uint32_t blk_row = (uint32_t)d * 32u;
   const __amdgpu_buffer_rsrc_t erc = buffer_rsrc(E, (uint32_t)(((size_t)V + 15) / 16 * blk_row));
@@ -740,8 +760,8 @@ __global__ void __launch_bounds__(256, 1)
 
   u32x4 tra[2];
   auto tr_load = [&](const DG_LDS u16* tile, int c, int slot) {
-    const u32x2 a = lds_read_tr16(tile + tr_off[0] + 32 * c);
-    const u32x2 b = lds_read_tr16(tile + tr_off[1] + 32 * c);
+    const u32x2 a = lds_read_tr16(tile + tr_off[0] + 512 * c);
+    const u32x2 b = lds_read_tr16(tile + tr_off[1] + 512 * c);
     tra[slot] = u32x4{a[0], a[1], b[0], b[1]};
   };
   tr_load((const DG_LDS u16*)&Et[1][w][0][0], 0, 0);  // tile -3: zeros
@@ -953,8 +973,7 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
         for (int h = 0; h < 4; ++h) xch[w][h][xw] = lg[h];
       }
-      *(DG_LDS u32x2*)(tile + wr_a + 32 * c) = u32x2{e[0], e[1]};
-      *(DG_LDS u32x2*)(tile + wr_b + 32 * c) = u32x2{e[2], e[3]};
+      *(DG_LDS u32x4*)(tile + wr + 512 * c) = e;
       if (c == 7 && own_ok) {
         // the other half's partial of tile t-1 (stored at chunk 3 of this
         // iteration), consumed at chunk 4 of the next
