@@ -55,6 +55,7 @@ __global__ void __launch_bounds__(256, 2)
   const int M = C * G;
   const int row = rb * 128 + w * 32 + l32;
   const bool rok = row < M;
+  const bool wave_live = rb * 128 + w * 32 < M;  // uniform over the wave
   const int qi = rok ? row / G : 0, qh = g * G + (rok ? row % G : 0);
   const u32x4 z4 = {0u, 0u, 0u, 0u};
 
@@ -141,95 +142,98 @@ __global__ void __launch_bounds__(256, 2)
     const int buf = t & 1;
     const int t0 = k_begin + t * 64;
     if (t + 1 < ntiles) load_tile(t0 + 64);
-
-    // S^T for keys 0..31 and 32..63: two independent chains interleaved, K
-    // fragments read two steps ahead of their products
-    f32x16 sacc[2] = {zero16(), zero16()};
-    {
-      u32x4 ka[3][2];
-      auto kread = [&](int ks) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) ka[ks % 3][kb] = *(const u32x4*)&Ks[buf][kb * 32 + l32][ks * 16 + h * 8];
-      };
-      kread(0);
-      kread(1);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 2 < KS) kread(ks + 2);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(ka[ks % 3][kb], qf[ks], sacc[kb]);
+    // a wave whose 32 packed rows are all past the canvas (few queries per
+    // KV head) only helps move the tiles: no products, no softmax
+    if (wave_live) {
+      // S^T for keys 0..31 and 32..63: two independent chains interleaved, K
+      // fragments read two steps ahead of their products
+      f32x16 sacc[2] = {zero16(), zero16()};
+      {
+        u32x4 ka[3][2];
+        auto kread = [&](int ks) {
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb) ka[ks % 3][kb] = *(const u32x4*)&Ks[buf][kb * 32 + l32][ks * 16 + h * 8];
+        };
+        kread(0);
+        kread(1);
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 2 < KS) kread(ks + 2);
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(ka[ks % 3][kb], qf[ks], sacc[kb]);
+        }
       }
-    }
-    // scores stay unscaled: p = 2^(s sl2 - m) with m in the scaled (log2) domain
-    if (!(t0 + 64 <= k_end && (!causal || t0 + 63 <= L))) {
-      // a ragged or causal tile (uniform branch): masked keys get -inf
-#pragma unroll
+      // scores stay unscaled: p = 2^(s sl2 - m) with m in the scaled (log2) domain
+      if (!(t0 + 64 <= k_end && (!causal || t0 + 63 <= L))) {
+        // a ragged or causal tile (uniform branch): masked keys get -inf
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = t0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+            const bool valid = key < k_end && (!causal || key <= qlim);
+            sacc[kb][e] = valid ? sacc[kb][e] : -INFINITY;
+          }
+      }
+      float tmax = -INFINITY;
+  #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = t0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-          const bool valid = key < k_end && (!causal || key <= qlim);
-          sacc[kb][e] = valid ? sacc[kb][e] : -INFINITY;
-        }
-    }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(sacc[kb][e], sacc[kb][e + 1]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;  // sl2 > 0 keeps the order
-    // Lazy reference: it moves only when a score exceeds it by more than
-    // kAttnLazy (log2 units), so p <= 2^kAttnLazy and the accumulators are
-    // rescaled a few times per row instead of on most tiles.
-    if (tmax > m + kAttnLazy) {
-      const float alpha = __builtin_amdgcn_exp2f(m - tmax);  // m = -inf gives 0
-      lsum *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
-      m = tmax;
-    }
-    // a row with no valid key yet keeps m = -inf: its scores are all -inf
-    const float mu = m == -INFINITY ? 0.f : m;
-    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-    typedef float f32x2v __attribute__((ext_vector_type(2)));
-    const bf16x2v one2 = __builtin_bit_cast(bf16x2v, 0x3f803f80u);  // (1, 1)
-    u32x4 pf[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float s0 = sacc[q >> 1][8 * (q & 1) + e], s1 = sacc[q >> 1][8 * (q & 1) + e + 1];
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s0, sl2, -mu)), p1 = __builtin_amdgcn_exp2f(fmaf(s1, sl2, -mu));
-        // P enters the product in bf16: the normaliser sums the same rounded
-        // values (a dot product of the packed pair with (1, 1))
-        const bf16x2v pb = __builtin_convertvector(f32x2v{p0, p1}, bf16x2v);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, one2, lsum, false);
-        pk[e >> 1] = __builtin_bit_cast(uint32_t, pb);
+  #pragma unroll
+        for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(sacc[kb][e], sacc[kb][e + 1]));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;  // sl2 > 0 keeps the order
+      // Lazy reference: it moves only when a score exceeds it by more than
+      // kAttnLazy (log2 units), so p <= 2^kAttnLazy and the accumulators are
+      // rescaled a few times per row instead of on most tiles.
+      if (tmax > m + kAttnLazy) {
+        const float alpha = __builtin_amdgcn_exp2f(m - tmax);  // m = -inf gives 0
+        lsum *= alpha;
+  #pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+        m = tmax;
       }
-      pf[q] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-    }
-    // O^T += V^T P^T: the MB output chains interleaved, V^T fragments of the
-    // next key group read one step ahead of their products
-    const DG_LDS u16* vbase = (const DG_LDS u16*)&Vs[buf][0][0];
-    {
-      u32x4 va[2][MB];
-      auto vread = [&](int q) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int r0 = 16 * q + 4 * h + ((l & 15) >> 2);
-          const int c0 = mb * 32 + 16 * ((l >> 4) & 1) + (l & 3) * 4;
-          const u32x2 a0 = lds_read_tr16(vbase + r0 * VP + c0);
-          const u32x2 a1 = lds_read_tr16(vbase + (r0 + 8) * VP + c0);
-          va[q & 1][mb] = u32x4{a0[0], a0[1], a1[0], a1[1]};
-        }
-      };
-      vread(0);
-#pragma unroll
+      // a row with no valid key yet keeps m = -inf: its scores are all -inf
+      const float mu = m == -INFINITY ? 0.f : m;
+      typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+      typedef float f32x2v __attribute__((ext_vector_type(2)));
+      const bf16x2v one2 = __builtin_bit_cast(bf16x2v, 0x3f803f80u);  // (1, 1)
+      u32x4 pf[4];
+  #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (q + 1 < 4) vread(q + 1);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) oacc[mb] = mfma32(va[q & 1][mb], pf[q], oacc[mb]);
+        uint32_t pk[4];
+  #pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float s0 = sacc[q >> 1][8 * (q & 1) + e], s1 = sacc[q >> 1][8 * (q & 1) + e + 1];
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s0, sl2, -mu)), p1 = __builtin_amdgcn_exp2f(fmaf(s1, sl2, -mu));
+          // P enters the product in bf16: the normaliser sums the same rounded
+          // values (a dot product of the packed pair with (1, 1))
+          const bf16x2v pb = __builtin_convertvector(f32x2v{p0, p1}, bf16x2v);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, one2, lsum, false);
+          pk[e >> 1] = __builtin_bit_cast(uint32_t, pb);
+        }
+        pf[q] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      }
+      // O^T += V^T P^T: the MB output chains interleaved, V^T fragments of the
+      // next key group read one step ahead of their products
+      const DG_LDS u16* vbase = (const DG_LDS u16*)&Vs[buf][0][0];
+      {
+        u32x4 va[2][MB];
+        auto vread = [&](int q) {
+  #pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const int r0 = 16 * q + 4 * h + ((l & 15) >> 2);
+            const int c0 = mb * 32 + 16 * ((l >> 4) & 1) + (l & 3) * 4;
+            const u32x2 a0 = lds_read_tr16(vbase + r0 * VP + c0);
+            const u32x2 a1 = lds_read_tr16(vbase + (r0 + 8) * VP + c0);
+            va[q & 1][mb] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+          }
+        };
+        vread(0);
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q + 1 < 4) vread(q + 1);
+  #pragma unroll
+          for (int mb = 0; mb < MB; ++mb) oacc[mb] = mfma32(va[q & 1][mb], pf[q], oacc[mb]);
+        }
       }
     }
     if (t + 1 < ntiles) store_tile(buf ^ 1);
