@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from oracle import step
-from synth import CONFIGS, Config, gen_problem, tau_schedule
+from synth import config_by_name, Config, gen_problem, tau_schedule
 from tests.gpu_util import ATOL, RELF, as_f64, close, close_rel, f64, need_gpu, renoise_match, say, top2_gap
 
 pytestmark = pytest.mark.gpu
@@ -160,7 +160,7 @@ def test_block_loop_graph_full_size():
     for bit, the appended cache rows of block 0 match the oracle's append of
     the GPU's finished canvas, and every step's outputs are valid."""
     import uniform_state_discrete_amd as dg
-    c = CONFIGS[4]
+    c = config_by_name("blocks4_canvas8x256_L4096_d2048_V262144")
     say(f"full-size block loop graph {c.name}")
     p = gen_problem(c)
     blocks, steps = 2, 2

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from oracle import step
-from synth import CONFIGS, Config, gen_problem
+from synth import config_by_name, Config, gen_problem
 from tests.gpu_util import ATOL, RELF, TAU_BAND, argmax_match, as_f64, close, f64, need_gpu, say, top2_gap
 
 pytestmark = pytest.mark.gpu
@@ -55,8 +55,8 @@ def tiny(cfg, name, idx, tau):
                   (tau, tau))
 
 
-@pytest.mark.parametrize("cfg", [tiny(CONFIGS[0], "masked_tiny", 95, 0.3), SMALL_BF16,
-                                 tiny(CONFIGS[1], "masked_v32768", 96, 0.9)], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [tiny(config_by_name("tiny_c16_L32_d64_V512_f32"), "masked_tiny", 95, 0.3), SMALL_BF16,
+                                 tiny(config_by_name("canvas256_L1024_d2048_V32768"), "masked_v32768", 96, 0.9)], ids=lambda c: c.name)
 def test_masked_step_lockstep(cfg):
     import uniform_state_discrete_amd as dg
     say(f"masked step lockstep {cfg.name}")
@@ -119,7 +119,7 @@ def test_masked_step_full_vocab_properties():
     every commit is a masked row whose own confidence met tau, it takes the
     row's argmax, and committed rows stay locked on the next step."""
     import uniform_state_discrete_amd as dg
-    c = CONFIGS[2]
+    c = config_by_name("canvas256_L8192_d2048_V262144")
     say(f"masked step full vocab {c.name}")
     p = gen_problem(c)
     Wd = {k: dg.to_device(v) for k, v in p.W.items()}

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from oracle import numerics, philox, step
-from synth import CONFIGS, Config, gen_problem, tau_schedule
+from synth import config_by_name, Config, gen_problem, tau_schedule
 from tests.gpu_util import (ATOL, RELF, argmax_match, as_f64, close, close_rel, dev, f64, need_gpu,
                             renoise_match, say, top2_gap)
 
@@ -100,7 +100,7 @@ def compare_full(c, o, ref, E, tau, tag):
                   ref["x_new"], ref["mask"], ref["c"], tau, extra_excl=tie)
 
 
-@pytest.mark.parametrize("cfg", [CONFIGS[0], SMALL_BF16, CONFIGS[1]], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [config_by_name("tiny_c16_L32_d64_V512_f32"), SMALL_BF16, config_by_name("canvas256_L1024_d2048_V32768")], ids=lambda c: c.name)
 def test_step_lockstep_every_element(cfg):
     import uniform_state_discrete_amd as dg
     say(f"step lockstep {cfg.name}")
@@ -182,10 +182,11 @@ def compare_rows(c, o, ref, rows, tau, tag):
     assert np.all(cf[keep] >= np.float32(tau)) and np.all(cf[~keep] < np.float32(tau))
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4])
-def test_step_full_size_sampled_rows(idx):
+@pytest.mark.parametrize("name", ["canvas256_L8192_d2048_V262144", "canvas256_L32768_d4096_V262144",
+                                  "blocks4_canvas8x256_L4096_d2048_V262144"])
+def test_step_full_size_sampled_rows(name):
     import uniform_state_discrete_amd as dg
-    c = CONFIGS[idx]
+    c = config_by_name(name)
     say(f"full-size step {c.name}")
     p = gen_problem(c)
     g = Dev(p)
@@ -194,7 +195,7 @@ def test_step_full_size_sampled_rows(idx):
     taus = tau_schedule(c)
     x = torch.empty((c.B, c.C), dtype=torch.int32, device="cuda")
     dg.dg_init_canvas(c.R, c.C, c.V, c.seed, 0, x)
-    rng = np.random.default_rng(idx)
+    rng = np.random.default_rng(c.index)
     rows = np.unique(np.concatenate([[0, 31, 32, c.R - 1], rng.integers(0, c.R, 8)]))
     S = None
     for s in range(2):
@@ -204,7 +205,7 @@ def test_step_full_size_sampled_rows(idx):
         x, S = o["tokens_out"], o["selfcond_out"]
 
 
-@pytest.mark.parametrize("cfg", [CONFIGS[0], SMALL_BF16], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [config_by_name("tiny_c16_L32_d64_V512_f32"), SMALL_BF16], ids=lambda c: c.name)
 def test_block_append_and_next_block(cfg):
     """Finish block 0, append it through the causal prefill, then run a step of
     block 1 against the grown cache."""

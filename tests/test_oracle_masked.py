@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from oracle import brute, step
-from synth import CONFIGS, Config, from_storage, gen_problem
+from synth import config_by_name, Config, from_storage, gen_problem
 
 M = 9  # the [MASK] id of the hand-worked cases
 
@@ -58,7 +58,7 @@ def test_unmask_threshold_extremes():
 
 
 def tiny_masked_cfg():
-    c = CONFIGS[0]
+    c = config_by_name("tiny_c16_L32_d64_V512_f32")
     return Config("tiny_masked", 93, c.B, c.C, c.L, c.d, c.Hq, c.Hkv, c.dh, c.V, c.dtype, 6, 1,
                   (0.3, 0.3))
 

@@ -11,7 +11,7 @@ import scipy.stats
 import torch
 
 from oracle import brute, numerics, philox, step
-from synth import CONFIGS, from_storage, gen_problem
+from synth import config_by_name, from_storage, gen_problem
 
 rng0 = np.random.default_rng(12345)
 
@@ -280,7 +280,7 @@ def _compare_step(ref, br, rel=1e-12):
 
 
 def test_step_matches_brute_force_tiny_workload():
-    cfg = CONFIGS[0]
+    cfg = config_by_name("tiny_c16_L32_d64_V512_f32")
     p = gen_problem(cfg)
     f = lambda a: from_storage(a, cfg.dtype).astype(np.float64)
     E, H, Kc, Vc = f(p.E), f(p.H[0]), f(p.Kc), f(p.Vc)
