@@ -229,6 +229,48 @@ def crossover_sweep(stream, reps=10):
     return out
 
 
+def prompt_prefill(stream, cfg, W, H_row, n=4096, reps=5):
+    """Causal prefill of an n-token prompt into an empty cache
+    (dg_prefill_append with L = 0, C = n) on the bench model: assemble, Q/K/V
+    projections, cache write and causal attention.  Beside it, the same
+    attention shape with no mask (every key tile), to show what the causal
+    key limit saves."""
+    import torch
+    import uniform_state_discrete_amd as dg
+    Hq, Hkv, dh, d = cfg.Hq, cfg.Hkv, cfg.dh, cfg.d
+    dims = dg.make_dims(1, n, 0, n, d, Hq, Hkv, dh, cfg.V, dg.DG_BF16)
+    ws = dg.workspace(dg.dg_workspace_bytes(dims))
+    Kc = torch.empty((1, Hkv, n, dh), dtype=torch.bfloat16, device="cuda")
+    Vc = torch.empty_like(Kc)
+    H = H_row.reshape(-1, d)[:1].expand(n, d).contiguous()   # hidden rows of the prompt
+    g = torch.Generator(device="cuda").manual_seed(4096)
+    toks = torch.randint(0, cfg.V, (1, n), generator=g, device="cuda", dtype=torch.int32)
+    attn = torch.empty((1, n, Hq, dh), dtype=torch.bfloat16, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = timed(lambda: dg.dg_prefill_append(dims, W, H, toks, Kc, Vc, attn, ws, stream))
+    q = torch.randn((1, n, Hq, dh), generator=g, device="cuda").to(torch.bfloat16)
+    kn = Kc.transpose(1, 2).contiguous()
+    vn = Vc.transpose(1, 2).contiguous()
+    wa = dg.workspace(dg.dg_attn_workspace_bytes(dims))
+    ms_causal = timed(lambda: dg.dg_attn_bidir(dims, q, Kc, Vc, kn, vn, attn, None, 1, wa, stream))
+    ms_full = timed(lambda: dg.dg_attn_bidir(dims, q, Kc, Vc, kn, vn, attn, None, 0, wa, stream))
+    fl = 2.0 * n * d * (Hq + 2 * Hkv) * dh + 2.0 * n * (n + 1) * Hq * dh   # projections + causal attention
+    return {"prompt_tokens": n, "ms": round(ms, 4), "tokens_per_s": round(n / (ms * 1e-3), 1),
+            "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "causal_attention_ms": round(ms_causal, 4), "unmasked_attention_ms": round(ms_full, 4)}
+
+
 def copy_calibration(mib):
     """A plain device-to-device copy of known size, for scaling HBM counters."""
     import torch
@@ -250,6 +292,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn-hbm", action="store_true", help="skip the HBM-bound attention shape")
     ap.add_argument("--no-block-loop", action="store_true", help="skip the block-diffusion graph replay")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the causal prompt prefill")
     ap.add_argument("--sweep-rows", action="store_true",
                     help="only run the rows sweep of the vocabulary head and attention (one JSON line per size)")
     ap.add_argument("--copy-mib", type=int, default=0, help="only run a plain copy of this size")
@@ -372,6 +415,8 @@ def main():
     }
     if not args.no_attn_hbm:
         out["attention_hbm_shape"] = attention_hbm_shape(stream)
+    if not args.no_prefill:
+        out["prompt_prefill"] = prompt_prefill(stream, cfg, W, H)
     if not args.no_block_loop:
         out["block_loop_graph"] = block_loop_graph(torch.cuda.Stream())
     if not args.no_cpu_baseline:

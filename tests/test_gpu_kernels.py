@@ -223,6 +223,9 @@ def _run_attn(B, C, L, cap, Hq, Hkv, dh, dtype, arrs, causal):
     (1, 50, 0, 8, 2, 128, "bf16", 3.0),        # empty cache, GQA 4
     (3, 70, 333, 4, 4, 128, "bf16", 2.0),      # MHA
     (1, 256, 1024, 16, 8, 128, "bf16", 1.0),   # the 32k-vocab step's attention shape
+    (1, 300, 0, 8, 2, 128, "bf16", 2.0),       # 10 row blocks x 3 splits: causal blocks skip splits
+    (2, 200, 150, 4, 2, 64, "bf16", 1.0),      # causal key limit inside a split, non-empty cache
+    (1, 40, 20, 2, 1, 32, "f32", 1.0),         # fp32 rows stop at their own key limit
 ])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_attention_matches_oracle(B, C, L, Hq, Hkv, dh, dtype, qscale, causal):

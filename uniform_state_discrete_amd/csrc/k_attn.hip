@@ -50,9 +50,13 @@ __global__ void __launch_bounds__(256, 2)
   bid /= nsplit;
   const int g = bid % Hkv, b = bid / Hkv;
   const int nkeys = L + C;
-  const int k_begin = split * kps;
-  const int k_end = min(nkeys, k_begin + kps);
   const int M = C * G;
+  // causal: no query of this row block sees a key past L + (its last query's
+  // position), so the block's key range stops there; a split beyond it has
+  // no tiles and leaves an empty partial (m = -inf, l = 0)
+  const int k_lim = causal ? min(nkeys, L + (min(M, rb * 128 + 128) - 1) / G + 1) : nkeys;
+  const int k_begin = split * kps;
+  const int k_end = min(k_lim, k_begin + kps);
   const int row = rb * 128 + w * 32 + l32;
   const bool rok = row < M;
   const bool wave_live = rb * 128 + w * 32 < M;  // uniform over the wave
@@ -346,7 +350,7 @@ __global__ void __launch_bounds__(256) k_attn_f32(int B, int C, int L, int cap, 
   if (tid < dh) qs[tid] = (double)Q[(size_t)r * dh + tid];
   __syncthreads();
   const double scale = 1.0 / sqrt((double)dh);
-  const int nkeys = L + C;
+  const int nkeys = causal ? L + i + 1 : L + C;  // causal: keys past L + i are masked
   double m = -INFINITY, lsum = 0.0, oacc = 0.0;
   for (int j0 = 0; j0 < nkeys; j0 += 256) {
     const int j = j0 + tid;
