@@ -169,18 +169,17 @@ int enqueue_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io,
     return hip_fail(e, "attention");
   if ((e = dg::launch_gemm_nt(dt, R, d, Hq * dh, O, w->Wo, X, Z, s)) != hipSuccess) return hip_fail(e, "output projection");
   dg::VocabPlan vp = dg::vocab_plan(R, d, dims->V, dt);
+  // the uniform-state renoise rides on the vocabulary head's split combine
+  const dg::RenoiseArgs rn{io->tokens_out, io->mask, tau, seed, t, block, dims->C, dims->V};
   if ((e = dg::launch_vocab(vp, Z, dt == DG_BF16 ? w->E_tiled : w->E, io->max_logit, io->argmax, io->conf, io->lse, io->selfcond_out,
-                            scratch, s, (hipEvent_t)io->ev_vocab_begin, (hipEvent_t)io->ev_vocab_end)) != hipSuccess)
-    return hip_fail(e, "vocab/self-conditioning");
+                            scratch, s, (hipEvent_t)io->ev_vocab_begin, (hipEvent_t)io->ev_vocab_end,
+                            mask_id >= 0 ? nullptr : &rn)) != hipSuccess)
+    return hip_fail(e, "vocab/self-conditioning/renoise");
   if (mask_id >= 0) {
     if ((e = dg::launch_unmask(R, io->argmax, io->conf, tau, mask_id, io->tokens_in, io->tokens_out, io->mask,
                                s)) != hipSuccess)
       return hip_fail(e, "unmask");
-    return DG_OK;
   }
-  if ((e = dg::launch_renoise(R, dims->C, dims->V, io->argmax, io->conf, tau, seed, t, block,
-                              io->tokens_out, io->mask, s)) != hipSuccess)
-    return hip_fail(e, "renoise");
   return DG_OK;
 }
 

@@ -58,6 +58,48 @@ __device__ __forceinline__ f32x16 zero16() {
 
 __device__ __forceinline__ u32x4 ldg128(const u16* p) { return *(const u32x4*)p; }
 
+// ---------------------------------------------------------------------------
+// Philox4x64-10 (Salmon et al., SC'11, "Parallel random numbers: as easy as
+// 1, 2, 3"): 10 rounds of two 64x64->128 multiplies with the round constants
+// below, the key bumped by the Weyl constants between rounds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t philox4x64_w0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                              uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += W0; k1 += W1; }
+    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+  }
+  return c0;
+}
+
+// The uniform-state renoise of one row (explainer, "Diffusione dello stato
+// uniforme"): conf < tau draws floor(w0 V / 2^64) from Philox4x64-10 at
+// counter (position, t, canvas, block), key (seed, 0); else the argmax.
+struct RenoiseArgs {
+  int32_t* out;    // NULL: no renoise
+  uint8_t* mask;   // may be NULL
+  float tau;
+  uint64_t seed;
+  uint32_t t, block;
+  int canvas, V;
+};
+__device__ __forceinline__ void renoise_row(const RenoiseArgs& rn, int r, int32_t argmax, float conf) {
+  const bool draw = conf < rn.tau;
+  int tok = argmax;
+  if (draw) {
+    const uint32_t b = (uint32_t)(r / rn.canvas), i = (uint32_t)(r % rn.canvas);
+    tok = (int)__umul64hi(philox4x64_w0(i, rn.t, b, rn.block, rn.seed, 0), (uint64_t)rn.V);
+  }
+  rn.out[r] = tok;
+  if (rn.mask) rn.mask[r] = draw ? 1 : 0;
+}
+
 }  // namespace dg
 
 // Launch wrappers (host side), implemented next to their kernels.  Each returns
@@ -70,9 +112,13 @@ struct VocabPlan {
 };
 VocabPlan vocab_plan(int rows, int d, int V, int dtype);
 // ev_begin / ev_end (may be NULL) are recorded around the main kernel only.
+// rn (may be NULL): the uniform-state renoise of every row, done by the split
+// combine from the row's own argmax and confidence (a separate launch on the
+// fp32 path, which has no combine).
 hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float* max_logit,
                         int32_t* argmax, float* conf, float* lse, void* selfcond, void* ws,
-                        hipStream_t s, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
+                        hipStream_t s, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr,
+                        const RenoiseArgs* rn = nullptr);
 
 struct AttnPlan {
   int B, C, L, cap, Hq, Hkv, dh, dtype, causal, nrb, nsplit, keys_per_split;

@@ -66,26 +66,6 @@ hipError_t launch_assemble(int dtype, int R, int d, int V, const void* H, const 
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Philox4x64-10 (Salmon et al., SC'11, "Parallel random numbers: as easy as
-// 1, 2, 3"): 10 rounds of two 64x64->128 multiplies with the round constants
-// below, the key bumped by the Weyl constants between rounds.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t philox_w0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
-                                              uint64_t k0, uint64_t k1) {
-  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r) { k0 += W0; k1 += W1; }
-    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
-    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
-    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
-  }
-  return c0;
-}
-
 // Uniform-state renoise (explainer, "Diffusione dello stato uniforme"): a
 // position whose confidence is below tau gets a fresh uniform vocabulary
 // token; the others take the argmax.  conf == NULL draws every position
@@ -95,19 +75,14 @@ __global__ void k_renoise(int rows, int canvas, int V, const int32_t* __restrict
                           uint32_t block, int32_t* __restrict__ out, uint8_t* __restrict__ mask) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= rows) return;
-  const bool draw = (conf == nullptr) || (conf[r] < tau);
-  int tok;
-  if (draw) {
-    const uint32_t b = (uint32_t)(r / canvas), i = (uint32_t)(r % canvas);
-    const uint64_t w0 = philox_w0(i, t, b, block, seed, 0);
-    tok = (int)__umul64hi(w0, (uint64_t)V);
-  } else {
-    tok = argmax[r];
+  const RenoiseArgs rn{out, mask, tau, seed, t, block, canvas, V};
+  if (conf == nullptr) {
+    // every position draws (conf = -inf is below any tau)
+    renoise_row(rn, r, 0, -INFINITY);
+    return;
   }
-  out[r] = tok;
-  if (mask) mask[r] = draw ? 1 : 0;
+  renoise_row(rn, r, argmax[r], conf[r]);
 }
-
 hipError_t launch_renoise(int rows, int canvas, int V, const int32_t* argmax, const float* conf,
                           float tau, uint64_t seed, uint32_t t, uint32_t block, int32_t* out,
                           uint8_t* mask, hipStream_t s) {

@@ -1049,7 +1049,7 @@ __global__ void __launch_bounds__(256) k_vocab_combine(int R, int d, int nsplit,
                                                        int32_t* __restrict__ argmax,
                                                        float* __restrict__ conf, float* __restrict__ lse,
                                                        void* __restrict__ S, int out_bf16,
-                                                       const uint32_t* __restrict__ err) {
+                                                       const uint32_t* __restrict__ err, RenoiseArgs rn) {
   __shared__ float wgt[1024];
   __shared__ float sh[4];
   const int r = blockIdx.x;
@@ -1060,6 +1060,7 @@ __global__ void __launch_bounds__(256) k_vocab_combine(int R, int d, int nsplit,
       argmax[r] = -1;
       conf[r] = NAN;
       if (lse) lse[r] = NAN;
+      if (rn.out) renoise_row(rn, r, -1, NAN);   // NaN is never below tau: token -1
     }
     for (int e = threadIdx.x; e < d; e += 256) {
       if (out_bf16) ((u16*)S)[(size_t)r * d + e] = 0x7FC0;
@@ -1101,8 +1102,10 @@ __global__ void __launch_bounds__(256) k_vocab_combine(int R, int d, int nsplit,
       sh[0] = 1.f / Lt;
       max_logit[r] = M;
       argmax[r] = A;
-      conf[r] = expf(M - mu) / Lt;
+      const float cf = expf(M - mu) / Lt;
+      conf[r] = cf;
       if (lse) lse[r] = mu + logf(Lt);
+      if (rn.out) renoise_row(rn, r, A, cf);   // the stored confidence decides
     }
   }
   __syncthreads();
@@ -1302,14 +1305,19 @@ VocabPlan vocab_plan(int rows, int d, int V, int dtype) {
 
 hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float* max_logit,
                         int32_t* argmax, float* conf, float* lse, void* selfcond, void* ws,
-                        hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end) {
+                        hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, const RenoiseArgs* rn) {
   if (p.rows <= 0) return hipSuccess;
   if (p.variant == 0) {
     hipLaunchKernelGGL(k_vocab_f32, dim3(p.rows), dim3(256), 0, s, p.rows, p.d, p.V,
                        (const float*)z, (const float*)E, max_logit, argmax, conf, lse,
                        (float*)selfcond);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && rn && rn->out)
+      e = launch_renoise(p.rows, rn->canvas, rn->V, argmax, conf, rn->tau, rn->seed, rn->t, rn->block, rn->out,
+                         rn->mask, s);
+    return e;
   }
+  const RenoiseArgs no_rn{nullptr, nullptr, 0.f, 0, 0, 0, 1, 1};
   float* pS = (float*)ws;
   f32x4* pstat = (f32x4*)((char*)ws + p.part_S_bytes);
   const dim3 grid((unsigned)(p.nrb * p.nsplit));
@@ -1352,7 +1360,8 @@ hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float*
   if (e != hipSuccess) return e;
   if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_vocab_combine, dim3(p.rows), dim3(256), 0, s, p.rows, p.d, p.nsplit, pS,
-                     pstat, max_logit, argmax, conf, lse, selfcond, 1, xhdr ? xhdr + 8 : nullptr);
+                     pstat, max_logit, argmax, conf, lse, selfcond, 1, xhdr ? xhdr + 8 : nullptr,
+                     rn ? *rn : no_rn);
   return hipGetLastError();
 }
 
