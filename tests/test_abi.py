@@ -69,6 +69,17 @@ def test_workspace_sizes(L):
     assert L.dg_vocab_workspace_bytes(16, 64, 512, L.DG_F32) == 0
 
 
+@pytest.mark.parametrize("C,Lc,Hq,Hkv", [(16, 32768, 32, 8), (256, 1024, 16, 8), (5, 700, 6, 2)])
+def test_attention_workspace_holds_the_split_partials(L, C, Lc, Hq, Hkv):
+    """Keys this long are split over several workgroups; every split leaves
+    an fp32 partial row (dh outputs, max and sum) per query head, so the
+    workspace holds at least two of them (one and several row blocks per KV
+    head)."""
+    dh = 128
+    d = dims(C=C, L=Lc, cap=Lc + C, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=dh)
+    assert L.dg_attn_workspace_bytes(d) >= 2 * C * Hq * (dh + 2) * 4
+
+
 def _step(L, d, ws_bytes=1 << 40, null=(), weights_null=(), ws=FAKE):
     lib = L.lib()
     w = L.Weights(*[None if k in weights_null else FAKE for k in L.WEIGHT_FIELDS])

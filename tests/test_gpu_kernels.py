@@ -226,6 +226,11 @@ def _run_attn(B, C, L, cap, Hq, Hkv, dh, dtype, arrs, causal):
     (1, 300, 0, 8, 2, 128, "bf16", 2.0),       # 10 row blocks x 3 splits: causal blocks skip splits
     (2, 200, 150, 4, 2, 64, "bf16", 1.0),      # causal key limit inside a split, non-empty cache
     (1, 40, 20, 2, 1, 32, "f32", 1.0),         # fp32 rows stop at their own key limit
+    # at most 64 packed rows (one row block, half its waves idle)
+    (2, 13, 100, 4, 2, 64, "bf16", 1.0),       # 26 rows, one split of two tiles
+    (1, 16, 2000, 8, 2, 128, "bf16", 2.0),     # 64 rows, 16 splits, ragged last split
+    (3, 5, 700, 6, 2, 128, "bf16", 1.0),       # GQA 3, ragged last split
+    (1, 20, 40, 2, 1, 64, "bf16", 1.0),        # one tile, no split
 ])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_attention_matches_oracle(B, C, L, Hq, Hkv, dh, dtype, qscale, causal):
