@@ -122,6 +122,7 @@ hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float*
 
 struct AttnPlan {
   int B, C, L, cap, Hq, Hkv, dh, dtype, causal, nrb, nsplit, keys_per_split;
+  int merge_first;  // first canvas position whose rows the split combine merges
   size_t part_bytes;
 };
 AttnPlan attn_plan(int B, int C, int L, int cap, int Hq, int Hkv, int dh, int dtype, int causal);

@@ -6,6 +6,10 @@
 #include "dg_common.h"
 #include <math.h>
 
+#include <algorithm>
+#include <functional>
+#include <vector>
+
 namespace dg {
 
 // ---------------------------------------------------------------------------
@@ -24,6 +28,17 @@ namespace dg {
 // by 64 B so that the row-wise and the transposing reads are conflict-free.
 // ---------------------------------------------------------------------------
 constexpr float kAttnLazy = 8.0f;
+
+// Keys seen by the packed row block rb (128 rows): all L + C of them in
+// denoising; in a causal pass none past L + (the block's last query's
+// position), so the block's key range stops there.
+__host__ __device__ inline int attn_key_limit(int causal, int L, int C, int G, int rb) {
+  const int nkeys = L + C, M = C * G;
+  if (!causal) return nkeys;
+  const int last = (M < rb * 128 + 128 ? M : rb * 128 + 128) - 1;
+  const int lim = L + last / G + 1;
+  return lim < nkeys ? lim : nkeys;
+}
 
 template <int DH>
 __global__ void __launch_bounds__(256, 2)
@@ -44,17 +59,21 @@ __global__ void __launch_bounds__(256, 2)
   // first of them has fetched it.  The grid is padded to a multiple of 8.
   int bid = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   if (bid >= nrb * nsplit * Hkv * B) return;
-  const int rb = bid % nrb;
+  // causal: the last row blocks see the most keys; dispatched first, their
+  // splits finish while the short blocks' workgroups fill the freed slots
+  const int rb = causal ? nrb - 1 - bid % nrb : bid % nrb;
   bid /= nrb;
   const int split = bid % nsplit;
   bid /= nsplit;
   const int g = bid % Hkv, b = bid / Hkv;
-  const int nkeys = L + C;
   const int M = C * G;
-  // causal: no query of this row block sees a key past L + (its last query's
-  // position), so the block's key range stops there; a split beyond it has
-  // no tiles and leaves an empty partial (m = -inf, l = 0)
-  const int k_lim = causal ? min(nkeys, L + (min(M, rb * 128 + 128) - 1) / G + 1) : nkeys;
+  const int k_lim = attn_key_limit(causal, L, C, G, rb);
+  // A row block whose keys all lie in the first split writes its output
+  // directly; its other splits have nothing to do.  A longer one leaves a
+  // partial per split (an empty one, m = -inf and l = 0, for a split past
+  // its key limit) for the combine.
+  const bool direct = k_lim <= kps;
+  if (direct && split > 0) return;
   const int k_begin = split * kps;
   const int k_end = min(k_lim, k_begin + kps);
   const int row = rb * 128 + w * 32 + l32;
@@ -246,7 +265,7 @@ __global__ void __launch_bounds__(256, 2)
   lsum += __shfl_xor(lsum, 32);
   if (!rok) return;
   const size_t orow = ((size_t)b * C + qi) * Hq + qh;
-  if (nsplit == 1) {
+  if (direct) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -277,18 +296,37 @@ __global__ void __launch_bounds__(256, 2)
 }
 
 // Merge of the key splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
-// splits in a fixed order (deterministic).  One workgroup per (b, i, h) row.
+// splits in a fixed order (deterministic).  Rows (b, i, h) of the canvas
+// positions i >= first (the rows before are written directly); a row of a row
+// block that was written directly is skipped.
 constexpr int kAttnMaxSplits = 512;  // attn_plan makes at most 512 splits
+constexpr int kAttnFewSplits = 8;    // at most this many: k_attn_combine_few
 
-__global__ void __launch_bounds__(128) k_attn_combine_bf16(int nrows, int nsplit, int dh,
-                                                           const float* __restrict__ Opart,
-                                                           const float* __restrict__ mpart,
-                                                           const float* __restrict__ lpart,
-                                                           u16* __restrict__ O, float* __restrict__ lse_out) {
+__device__ __forceinline__ bool attn_merge_row(int ridx, int mrows, int C, int L, int Hq, int G, int causal,
+                                               int kps, int first, int& r) {
+  if (ridx >= mrows) return false;
+  const int span = (C - first) * Hq;
+  const int bb = ridx / span, rem = ridx % span;
+  const int i = first + rem / Hq, hq = rem % Hq;
+  r = (bb * C + i) * Hq + hq;
+  return attn_key_limit(causal, L, C, G, (i * G + hq % G) / 128) > kps;
+}
+
+// Many splits (few rows): one row per workgroup of 128 threads; one wave
+// computes the split weights into LDS, every thread then merges one feature.
+__global__ void __launch_bounds__(128)
+    k_attn_combine_bf16(int nrows, int mrows, int nsplit, int dh, int C, int L, int Hq, int G, int causal,
+                        int kps, int first, const float* __restrict__ Opart, const float* __restrict__ mpart,
+                        const float* __restrict__ lpart, u16* __restrict__ O, float* __restrict__ lse_out) {
   __shared__ float wgt[kAttnMaxSplits];
   __shared__ float sh[2];
-  const int r = blockIdx.x;
-  if (threadIdx.x < 64) {
+  const int ridx = blockIdx.x;
+  const int span = (C - first) * Hq;
+  const int bb = ridx / span, rem = ridx % span;
+  const int i = first + rem / Hq, hq = rem % Hq;
+  const bool live = ridx < mrows && attn_key_limit(causal, L, C, G, (i * G + hq % G) / 128) > kps;
+  const int r = (bb * C + i) * Hq + hq;
+  if (live && threadIdx.x < 64) {
     // one wave: lane l takes splits l, l+64, ...; fixed-pattern reductions
     const int l = threadIdx.x;
     float M = -INFINITY;
@@ -308,9 +346,10 @@ __global__ void __launch_bounds__(128) k_attn_combine_bf16(int nrows, int nsplit
     }
   }
   __syncthreads();
+  if (!live) return;
   const float inv = sh[0];
   // splits in a fixed order; 8 independent loads in flight per thread
-  for (int f = threadIdx.x; f < dh; f += blockDim.x) {
+  for (int f = threadIdx.x; f < dh; f += 128) {
     float acc = 0.f;
     const float* op = Opart + (size_t)r * dh + f;
     const size_t st = (size_t)nrows * dh;
@@ -326,6 +365,52 @@ __global__ void __launch_bounds__(128) k_attn_combine_bf16(int nrows, int nsplit
     O[(size_t)r * dh + f] = (u16)f32_to_bf16(acc * inv);
   }
   if (lse_out && threadIdx.x == 0) lse_out[r] = sh[1];
+}
+
+// Few splits (many rows): one row per wave, four per workgroup.  Every lane
+// issues all its loads at once (the split maxima and sums, and its dh / 64
+// features of every split), so a row costs one memory round trip; every lane
+// forms the same weights from the same values, with no LDS and no barrier.
+__global__ void __launch_bounds__(256)
+    k_attn_combine_few(int nrows, int mrows, int nsplit, int dh, int C, int L, int Hq, int G, int causal,
+                       int kps, int first, const float* __restrict__ Opart, const float* __restrict__ mpart,
+                       const float* __restrict__ lpart, u16* __restrict__ O, float* __restrict__ lse_out) {
+  int r = 0;
+  if (!attn_merge_row(blockIdx.x * 4 + (threadIdx.x >> 6), mrows, C, L, Hq, G, causal, kps, first, r)) return;
+  const int l = threadIdx.x & 63;
+  const size_t st = (size_t)nrows * dh;
+  float ms[kAttnFewSplits], ls[kAttnFewSplits], v[kAttnFewSplits][2];
+#pragma unroll
+  for (int s = 0; s < kAttnFewSplits; ++s) {
+    if (s < nsplit) {
+      ms[s] = mpart[(size_t)s * nrows + r];
+      ls[s] = lpart[(size_t)s * nrows + r];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        v[s][j] = 64 * j + l < dh ? Opart[(size_t)s * st + (size_t)r * dh + 64 * j + l] : 0.f;
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kAttnFewSplits; ++s)
+    if (s < nsplit) M = fmaxf(M, ms[s]);
+  float part = 0.f, acc[2] = {0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kAttnFewSplits; ++s) {
+    if (s < nsplit) {
+      const float ws = ms[s] == -INFINITY ? 0.f : exp2f(ms[s] - M);
+      if (ws != 0.f) {
+        part += ws * ls[s];
+        acc[0] += ws * v[s][0];
+        acc[1] += ws * v[s][1];
+      }
+    }
+  }
+  const float inv = part > 0.f ? 1.f / part : 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (64 * j + l < dh) O[(size_t)r * dh + 64 * j + l] = (u16)f32_to_bf16(acc[j] * inv);
+  if (lse_out && l == 0) lse_out[r] = (M + log2f(part)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -399,6 +484,57 @@ __global__ void __launch_bounds__(256) k_attn_f32(int B, int C, int L, int cap, 
 }
 
 // ---------------------------------------------------------------------------
+// Causal passes: row block rb sees about L + (rb + 1) 64 keys, so the last
+// blocks set the critical path.  Candidate split counts from ns0 up are
+// scored in units of one tile's time: list scheduling in dispatch order
+// (longest row blocks first, split by split), each XCD taking its eighth of
+// the grid on its own 64 slots (32 CUs, two workgroups each), with one tile
+// of fixed cost per workgroup that has keys, plus the partials'
+// write and read at kAttnTileBytes per tile time (the chip moves about
+// 12 MB from HBM in the ~3 us a workgroup spends on one tile).  The lowest
+// score wins, the fewest splits on a tie.
+constexpr double kAttnTileBytes = 12e6;
+static int attn_causal_splits(int B, int C, int L, int Hq, int Hkv, int G, int dh, int nrb, int ns0,
+                              int maxs) {
+  const int nkeys = L + C;
+  int best = ns0;
+  double best_span = 1e300;
+  std::vector<double> slot;
+  for (int ns = ns0; ns <= maxs && ns <= 4 * ns0; ++ns) {
+    const int kps = ((nkeys + ns - 1) / ns + 63) / 64 * 64;
+    const int nsp = (nkeys + kps - 1) / kps;
+    const long total = (long)nrb * nsp * Hkv * B, chunk = (total + 7) / 8;
+    // per XCD, a min-heap of the times at which its 64 slots come free
+    slot.assign(8 * 64, 0.0);
+    auto put = [&](int x, double len) {
+      auto b0 = slot.begin() + 64 * x, b1 = b0 + 64;
+      std::pop_heap(b0, b1, std::greater<double>());
+      *(b1 - 1) += len;
+      std::push_heap(b0, b1, std::greater<double>());
+    };
+    long idx = 0;
+    for (int bg = 0; bg < B * Hkv; ++bg)
+      for (int sp = 0; sp < nsp; ++sp)
+        for (int k = 0; k < nrb; ++k, ++idx) {
+          const int rb = nrb - 1 - k;
+          const int lim = attn_key_limit(1, L, C, G, rb);
+          const int kb = sp * kps, ke = lim < kb + kps ? lim : kb + kps;
+          const double len = (lim <= kps && sp > 0) ? 0.0 : (ke > kb ? 1.0 + (ke - kb + 63) / 64 : 0.25);
+          put((int)(idx / chunk), len);
+        }
+    int rb0 = 0;
+    while (rb0 < nrb && attn_key_limit(1, L, C, G, rb0) <= kps) ++rb0;
+    const double merged = nsp > 1 ? (double)B * (C - (rb0 < nrb ? rb0 * 128 / G : C)) * Hq : 0.0;
+    const double span = *std::max_element(slot.begin(), slot.end()) +
+                        2.0 * merged * nsp * (dh + 2) * 4.0 / kAttnTileBytes;
+    if (span < best_span) {
+      best_span = span;
+      best = ns;
+    }
+  }
+  return best;
+}
+
 AttnPlan attn_plan(int B, int C, int L, int cap, int Hq, int Hkv, int dh, int dtype, int causal) {
   AttnPlan p{};
   p.B = B; p.C = C; p.L = L; p.cap = cap; p.Hq = Hq; p.Hkv = Hkv; p.dh = dh; p.dtype = dtype;
@@ -411,12 +547,18 @@ AttnPlan attn_plan(int B, int C, int L, int cap, int Hq, int Hkv, int dh, int dt
     int ns = (512 + pairs - 1) / pairs;             // about two workgroups per CU
     const int maxs = (nkeys + 127) / 128;           // at least two 64-key tiles per split
     ns = ns < 1 ? 1 : (ns > maxs ? maxs : ns);
+    if (causal) ns = attn_causal_splits(B, C, L, Hq, Hkv, G, dh, p.nrb, ns, maxs);
     p.keys_per_split = ((nkeys + ns - 1) / ns + 63) / 64 * 64;
     p.nsplit = (nkeys + p.keys_per_split - 1) / p.keys_per_split;
     if (p.nsplit < 1) p.nsplit = 1;
-    p.part_bytes = p.nsplit > 1 ? (size_t)p.nsplit * B * C * Hq * (dh + 2) * sizeof(float) : 0;
+    // the first canvas position with a row in a split row block (row blocks
+    // past it see at least as many keys)
+    int rb0 = 0;
+    while (rb0 < p.nrb && attn_key_limit(causal, L, C, G, rb0) <= p.keys_per_split) ++rb0;
+    p.merge_first = rb0 < p.nrb ? rb0 * 128 / G : C;
+    p.part_bytes = p.merge_first < C ? (size_t)p.nsplit * B * C * Hq * (dh + 2) * sizeof(float) : 0;
   } else {
-    p.nrb = 1; p.nsplit = 1; p.keys_per_split = nkeys; p.part_bytes = 0;
+    p.nrb = 1; p.nsplit = 1; p.keys_per_split = nkeys; p.part_bytes = 0; p.merge_first = C;
   }
   return p;
 }
@@ -455,9 +597,16 @@ hipError_t launch_attn(const AttnPlan& p, const void* q, const void* kc, const v
 #undef DG_ATTN_LAUNCH
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev_end) e = hipEventRecord(ev_end, s);
-  if (e != hipSuccess || p.nsplit == 1) return e;
-  hipLaunchKernelGGL(k_attn_combine_bf16, dim3((unsigned)nrows), dim3(128), 0, s, (int)nrows,
-                     p.nsplit, p.dh, Opart, mpart, lpart, (u16*)out, lse);
+  if (e != hipSuccess || p.merge_first >= p.C) return e;
+  const size_t mrows = (size_t)p.B * (p.C - p.merge_first) * p.Hq;
+  if (p.nsplit <= kAttnFewSplits)
+    hipLaunchKernelGGL(k_attn_combine_few, dim3((unsigned)((mrows + 3) / 4)), dim3(256), 0, s, (int)nrows,
+                       (int)mrows, p.nsplit, p.dh, p.C, p.L, p.Hq, G, p.causal, p.keys_per_split,
+                       p.merge_first, Opart, mpart, lpart, (u16*)out, lse);
+  else
+    hipLaunchKernelGGL(k_attn_combine_bf16, dim3((unsigned)mrows), dim3(128), 0, s, (int)nrows,
+                       (int)mrows, p.nsplit, p.dh, p.C, p.L, p.Hq, G, p.causal, p.keys_per_split,
+                       p.merge_first, Opart, mpart, lpart, (u16*)out, lse);
   return hipGetLastError();
 }
 
