@@ -94,6 +94,8 @@ __global__ void __launch_bounds__(256, 2)
   float m = -INFINITY, lsum = 0.f;
   const float sl2 = kLog2e * rsqrtf((float)DH);
   const int qlim = L + qi;  // causal: key <= L + i
+  // causal: every row of the block sees keys up to L + (its first position)
+  const int kvis = L + rb * 128 / G;
 
   u32x4 kreg[NLD], vreg[NLD];
   // Tiles that lie in the cache and inside the split (all but the last one
@@ -187,8 +189,9 @@ __global__ void __launch_bounds__(256, 2)
         }
       }
       // scores stay unscaled: p = 2^(s sl2 - m) with m in the scaled (log2) domain
-      if (!(t0 + 64 <= k_end && (!causal || t0 + 63 <= L))) {
-        // a ragged or causal tile (uniform branch): masked keys get -inf
+      if (!(t0 + 64 <= k_end && (!causal || t0 + 63 <= kvis))) {
+        // a ragged tile or one that crosses the causal diagonal (uniform
+        // branch): masked keys get -inf
   #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
   #pragma unroll
