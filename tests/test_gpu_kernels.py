@@ -231,6 +231,9 @@ def _run_attn(B, C, L, cap, Hq, Hkv, dh, dtype, arrs, causal):
     (1, 16, 2000, 8, 2, 128, "bf16", 2.0),     # 64 rows, 16 splits, ragged last split
     (3, 5, 700, 6, 2, 128, "bf16", 1.0),       # GQA 3, ragged last split
     (1, 20, 40, 2, 1, 64, "bf16", 1.0),        # one tile, no split
+    # causal, GQA 3: row blocks 0-1 fit one split (written directly), row
+    # block 2 is split; position 85 has rows in both kinds of row block
+    (1, 100, 40, 6, 2, 64, "bf16", 1.0),
 ])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_attention_matches_oracle(B, C, L, Hq, Hkv, dh, dtype, qscale, causal):
