@@ -25,7 +25,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 DEFAULT_WORKLOAD = "canvas256_L8192_d2048_V262144"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_vocab_traffic.json")
 VOCAB_SOURCES = [os.path.join(ROOT, "uniform_state_discrete_amd", "csrc", f)
-                 for f in ("k_vocab.hip", "dg_common.h")]
+                 for f in ("k_vocab.hip", "vocab_common.h", "dg_common.h")] + [
+    os.path.join(ROOT, "uniform_state_discrete_amd", "build.py")]  # its flags shape the code
 
 
 def vocab_source_hash():
@@ -49,15 +50,16 @@ def algorithmic(cfg):
                 by_E=by_E, by_cache=by_cache, bytes=by_E + by_cache + by_w)
 
 
-def read_traffic():
+def read_traffic(workload):
     """HBM bytes per flash-vocab launch from the committed rocprofv3 counter
-    runs, or None when they were taken on a different kernel source."""
+    runs, or None when they were taken on a different kernel source or
+    another workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != vocab_source_hash():
+    if t.get("source_sha256") != vocab_source_hash() or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
 
@@ -380,7 +382,7 @@ def main():
 
     alg = algorithmic(cfg)
     achieved = alg["fl_vocab"] / (v_avg * 1e-3) / 1e12
-    traffic = read_traffic()
+    traffic = read_traffic(cfg.name)
     steps_s = 1000.0 / ms_step
     out = {
         "metric": "canvas denoise steps/s (256 tok, V=262144) + % MFMA peak, % HBM peak",

@@ -3,90 +3,9 @@
 // (DiffusionGemma explainer, "Autocondizionamento": the probability matrix
 // times the token-embedding table is handed to the next step), in one pass
 // over the embedding table E that never stores the rows x V probabilities.
-#include "dg_common.h"
-#include <math.h>
+#include "vocab_common.h"
 
 namespace dg {
-
-// Rescale threshold (natural-log units): a row's reference max only moves
-// when a new logit exceeds it by more than this.  P = exp(l - m_ref) then
-// stays <= e^40, and a sum of up to 2^24 such terms times |E| stays far below
-// FLT_MAX; terms more than ~87 below the reference underflow, and they are
-// then more than 87 below the row's maximum too (negligible in fp32).
-constexpr float kLazyTh = 40.0f;
-
-// LDS row of E-tile row m.  Rows are padded by 16 bytes, so the 64 banks see
-// (row + 16-byte unit) mod 16; permuting each group of 16 rows (even rows of
-// the group first, then odd) keeps both access patterns conflict-free: 16
-// lanes writing one 16-byte unit of 16 consecutive tile rows, and the
-// transposing reads of 8 consecutive tile rows x 32 bytes per 32 lanes.
-// Column offsets stay compile-time.
-__device__ __forceinline__ int prow16(int m) { return 2 * (m & 7) + (m >> 3); }
-
-typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4 mfma16x32(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16x16(u32x2 a, u32x2 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4v, a),
-                                                   __builtin_bit_cast(bf16x4v, b), c, 0, 0, 0);
-}
-
-// D += A.B on a 16x16x32 tile with D in VGPRs.  The products whose
-// accumulators live in the AGPR file (the self-conditioning sums fill all 256
-// of them) go through the builtin; the per-tile logits accumulate in VGPRs
-// through this form, so the register allocator never has to move
-// accumulators between the two files.  The compiler does not track the
-// hazards of inline assembly: the leading s_nop gives the 2 wait states a
-// product needs after a VALU write of any of its operands (the zeroed
-// accumulator at the start of a tile); a chain of these products on one
-// accumulator needs none; reads of the result by other instructions wait in
-// mfma_v_settle.
-__device__ __forceinline__ void mfma16x32_v(u32x4 a, u32x4 b, f32x4& d) {
-  asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-// The same product without the leading wait states, for operands that no
-// VALU instruction wrote (loaded from memory, constant, or the accumulator of
-// the chain itself), and the first product of a chain, whose accumulator
-// input is the inline constant 0 (no zeroing instructions, no wait states).
-__device__ __forceinline__ void mfma16x32_vn(u32x4 a, u32x4 b, f32x4& d) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma16x32_v0(u32x4 a, u32x4 b, f32x4& d) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
-}
-// Wait states between the last VGPR-form product and any other reader of its
-// result.
-__device__ __forceinline__ void mfma_v_settle(f32x4 (&lg)[2][2]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(lg[0][0]), "+v"(lg[0][1]), "+v"(lg[1][0]), "+v"(lg[1][1]));
-}
-__device__ __forceinline__ void mfma_v_settle(f32x4 (&lg)[4]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(lg[0]), "+v"(lg[1]), "+v"(lg[2]), "+v"(lg[3]));
-}
-__device__ __forceinline__ void mfma_v_settle(f32x4& a, f32x4& b) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
-}
-
-// The tiled table stores the 16 bytes of a lane with odd g (columns
-// 8g..8g+7 of a chunk) as columns 8g+4..8g+7 then 8g..8g+3: those lanes
-// write their first 8 bytes to LDS column 8g+4, the others to 8g, so each
-// LDS store instruction covers all 64 banks without selecting data.  The
-// matrix-core contraction sees the same permuted k-slots on both operands:
-// the Z fragments of odd-g lanes get their halves swapped once, at load.
-__device__ __forceinline__ u32x4 swap_halves(u32x4 v, bool sw) {
-  return sw ? u32x4{v[2], v[3], v[0], v[1]} : v;
-}
-
-// Workgroup -> (row block, vocab split).  Workgroups are dispatched round-robin
-// over the 8 XCDs (blockIdx % 8); consecutive linear ids are given to one XCD,
-// so the row blocks that share a vocab split share that XCD's L2.
-__device__ __forceinline__ void vocab_block(int nrb, int& rb, int& split) {
-  const int nblk = gridDim.x, bid = blockIdx.x;
-  const int lin = (nblk & 7) == 0 ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
-  split = lin / nrb;
-  rb = lin % nrb;
-}
 
 // ---------------------------------------------------------------------------
 // Variant 32 (d = 4*SLICE <= 2048).  Workgroup = 4 waves, 32 rows of Z, one
@@ -121,45 +40,6 @@ __device__ __forceinline__ void vocab_block(int nrb, int& rb, int& split) {
 // ever stored raw, so it stays in the AGPR file).  Output: G (unnormalised,
 // relative to the final m_seg) and per-row (m_seg, sum, max, argmax).
 // ---------------------------------------------------------------------------
-#ifndef DG_VOCAB32_PF
-#define DG_VOCAB32_PF 8
-#endif
-// Buffer resource over [base, base + bytes): loads past the end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 buffer_ld128(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-}
-// LDS row of a 16-row tile row m: the 16-lane writes of one 16-byte unit of 16
-// consecutive rows and the transposing reads of 4 rows x 4 units per 32 lanes
-// fall on distinct banks (rows are padded by 16 bytes).
-__device__ __forceinline__ int prow16t(int m) { return 4 * (m & 3) + (m >> 2); }
-// max with the lowest id on ties, and sums, over 8 consecutive lanes (DPP:
-// swap neighbours, swap pairs, mirror the two quads)
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& m, int& a) {
-  const float om = dpp_f<CTRL>(m);
-  const int oa = dpp_i<CTRL>(a);
-  const bool take = (om > m) | ((om == m) & (oa < a));  // branch-free
-  m = take ? om : m;
-  a = take ? oa : a;
-}
-__device__ __forceinline__ float sum8(float s) {
-  s += dpp_f<0xB1>(s);
-  s += dpp_f<0x4E>(s);
-  s += dpp_f<0x141>(s);
-  return s;
-}
-
 template <int SLICE>
 __global__ void __launch_bounds__(256, 1)
     k_vocab32(const u16* __restrict__ Z, const u16* __restrict__ E, int R, int d, int V, int nrb,
@@ -411,179 +291,6 @@ __global__ void __launch_bounds__(256, 1)
   const float tot = sum8(lsum);
   if (r0 + orow < R && q == 0)
     pstat[(size_t)split * R + r0 + orow] = f32x4{m_seg, tot, m_true, __int_as_float(amax)};
-}
-
-// ---------------------------------------------------------------------------
-// Variant 16 (d = 4*SLICE up to 4096): the same algorithm on 16-row tiles and
-// 16-id vocab tiles, so that one E tile (16 x d) fits in LDS at d = 4096.
-// Logits^T use 16x16x32 MFMAs; the P.E product uses 16x16x16 MFMAs, whose
-// 4-deep K slice lines up with the logits' output layout (no permutation).
-// ---------------------------------------------------------------------------
-template <int SLICE>
-__global__ void __launch_bounds__(256, 1)
-    k_vocab16(const u16* __restrict__ Z, const u16* __restrict__ E, int R, int d, int V, int nrb,
-              int split_len, float* __restrict__ pS, f32x4* __restrict__ pstat) {
-  constexpr int NCH = SLICE / 32, EP = SLICE + 8;
-  constexpr int PF = NCH < 8 ? NCH : 8;
-  __shared__ __attribute__((aligned(16))) u16 Et[4][16][EP];
-  __shared__ __attribute__((aligned(16))) f32x4 xch[4][64];
-
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g4 = l >> 4, l16 = l & 15;
-  int rb, split;
-  vocab_block(nrb, rb, split);
-  const int r0 = rb * 16;
-  const int vs = split * split_len, ve = min(V, vs + split_len);
-  const int dbase = w * SLICE;
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
-
-  const int zr = r0 + l16;
-  const bool zok = zr < R;
-  u32x4 zf[NCH];
-  {
-    const u16* zp = Z + (size_t)(zok ? zr : R - 1) * d + dbase + g4 * 8;
-#pragma unroll
-    for (int ks = 0; ks < NCH; ++ks) zf[ks] = swap_halves(ldg128(zp + ks * 32), g4 & 1);
-  }
-  float* gp = pS + ((size_t)split * R + (zok ? zr : 0)) * d + dbase + 4 * g4;
-  const size_t tofs = (size_t)gridDim.x / nrb * R * d;
-  DG_LDS u16* et = (DG_LDS u16*)&Et[w][0][0];
-  const int nt = ve > vs ? (ve - vs + 15) / 16 : 0;
-  for (int e = l * 8; e < 16 * EP; e += 64 * 8) *(DG_LDS u32x4*)(et + e) = z4;
-  const int tr_r = 4 * g4 + (l16 >> 2);
-  const DG_LDS u16* trb = et + prow16(tr_r) * EP + (l & 3) * 4;
-  DG_LDS u16* wrb = et + prow16(l16) * EP + g4 * 8;
-
-  // E is the tiled table (one 1 KiB block of 16 ids x 32 columns per load
-  // instruction, in operand lane order); ids past the table read zeros
-  const uint32_t blk_row = (uint32_t)d * 32u;
-  const __amdgpu_buffer_rsrc_t erc = buffer_rsrc(E, (uint32_t)(((size_t)V + 15) / 16 * blk_row));
-  const uint32_t lane_off = (uint32_t)((size_t)(vs / 16) * blk_row + (size_t)(dbase / 32) * 1024u + l * 16u);
-  u32x4 ring0[PF];
-  auto issue = [&](int slot, int tile, int c) {
-    ring0[slot] = buffer_ld128(erc, lane_off + (uint32_t)tile * blk_row + 1024u * c);
-  };
-#pragma unroll
-  for (int c = 0; c < PF; ++c) issue(c, 0, c);
-
-  float m_seg = -INFINITY, lsum = 0.f, m_G = -INFINITY, l_G = 0.f;
-  bool g_valid = false;
-  float m_true = -INFINITY, tmax = -INFINITY;
-  int amax = 0;
-  u32x2 pf = {0u, 0u};
-  float L[4];  // logits of ids v0 + 4*g4 + i of the current tile
-
-  auto gather_logits = [&](int v0, float* L) {
-    f32x4 a = xch[0][l];
-    a += xch[1][l];
-    a += xch[2][l];
-    a += xch[3][l];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) L[i] = (v0 + 4 * g4 + i) < ve ? a[i] : -INFINITY;  // id v0 + 4*g4 + i
-  };
-  auto make_p = [&](const float* L) {
-    float pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = L[i] == -INFINITY ? 0.f : exp2f((L[i] - m_seg) * kLog2e);
-      lsum += pv[i];
-    }
-    pf = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-  };
-
-  int t = 0;
-  for (;;) {
-    f32x4 acc[2 * NCH];
-#pragma unroll
-    for (int c = 0; c < 2 * NCH; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool rescale = false;
-    for (;; ++t) {
-      const bool have = t < nt;
-      f32x4 lg = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int slot = c % PF;
-        const u32x4 e0 = ring0[slot];
-        lg = mfma16x32(e0, zf[c], lg);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const u32x2 a = lds_read_tr16(trb + c * 32 + 16 * p);
-          acc[2 * c + p] = mfma16x16(a, pf, acc[2 * c + p]);
-        }
-        *(DG_LDS u32x2*)(wrb + c * 32 + ((g4 & 1) ? 4 : 0)) = u32x2{e0[0], e0[1]};
-        *(DG_LDS u32x2*)(wrb + c * 32 + ((g4 & 1) ? 0 : 4)) = u32x2{e0[2], e0[3]};
-        if (c + PF < NCH)
-          issue(slot, t, c + PF);
-        else
-          issue(slot, t + 1, c + PF - NCH);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (!have) break;
-
-      xch[w][l] = lg;
-      __syncthreads();
-      const int v0 = vs + t * 16;
-      gather_logits(v0, L);
-      __syncthreads();
-
-      tmax = -INFINITY;
-      int targ = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool gt = L[i] > tmax;
-        tmax = gt ? L[i] : tmax;
-        targ = gt ? v0 + 4 * g4 + i : targ;
-      }
-#pragma unroll
-      for (int o = 16; o <= 32; o <<= 1) {
-        const float om = __shfl_xor(tmax, o);
-        const int oa = __shfl_xor(targ, o);
-        const bool take = om > tmax || (om == tmax && oa < targ);
-        tmax = take ? om : tmax;
-        targ = take ? oa : targ;
-      }
-      amax = tmax > m_true ? targ : amax;
-      m_true = fmaxf(m_true, tmax);
-      if (m_seg == -INFINITY) {
-        m_seg = tmax;
-      } else if (__any(tmax > m_seg + kLazyTh)) {
-        rescale = true;
-        break;
-      }
-      make_p(L);
-    }
-
-    const float m_new = rescale ? fmaxf(m_seg, tmax) : m_seg;
-    float* dst = g_valid ? gp + tofs : gp;
-    if (zok) {
-#pragma unroll
-      for (int c = 0; c < 2 * NCH; ++c) *(f32x4*)(dst + 16 * c) = acc[c];
-    }
-    if (!g_valid) {
-      m_G = m_seg;
-      l_G = lsum;
-      g_valid = true;
-    } else {
-      const float gs = m_G == -INFINITY ? 0.f : exp2f((m_G - m_new) * kLog2e);
-      const float as = m_seg == -INFINITY ? 0.f : exp2f((m_seg - m_new) * kLog2e);
-      if (zok) {
-        for (int c = 0; c < 2 * NCH; ++c) {
-          float* g = gp + 16 * c;
-          *(f32x4*)g = *(const f32x4*)g * gs + *(const f32x4*)(g + tofs) * as;
-        }
-      }
-      l_G = l_G * gs + lsum * as;
-      m_G = m_new;
-    }
-    if (!rescale) break;
-    m_seg = m_new;
-    lsum = 0.f;
-    make_p(L);  // this tile's P against the new reference (L still holds it)
-    ++t;
-  }
-
-  l_G += __shfl_xor(l_G, 16);
-  l_G += __shfl_xor(l_G, 32);
-  if (zok && w == 0 && g4 == 0) pstat[(size_t)split * R + zr] = f32x4{m_G, l_G, m_true, __int_as_float(amax)};
 }
 
 // ---------------------------------------------------------------------------
@@ -1352,7 +1059,7 @@ hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float*
     }
   } else {
     switch (sl) {
-      case 1024: hipLaunchKernelGGL(k_vocab16<1024>, grid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb, p.split_len, pS, pstat); break;
+      case 1024: launch_vocab16_1024(grid, s, Zb, Eb, p.rows, p.d, p.V, p.nrb, p.split_len, pS, pstat); break;
       default: launched = false;
     }
   }
