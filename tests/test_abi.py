@@ -69,6 +69,27 @@ def test_workspace_sizes(L):
     assert L.dg_vocab_workspace_bytes(16, 64, 512, L.DG_F32) == 0
 
 
+@pytest.mark.parametrize("B,C,Lk,Hq,Hkv,dh", [
+    (1, 1, 0, 2, 1, 64), (1, 4096, 0, 16, 8, 128), (8, 256, 4096, 16, 8, 128),
+    (1, 16, 1 << 20, 32, 8, 128), (2, 32768, 0, 32, 8, 128), (3, 300, 77, 12, 4, 64),
+    (1, 100, 40, 6, 2, 64)])
+def test_attention_plan_bounds(L, B, C, Lk, Hq, Hkv, dh):
+    """The host plan of the bf16 attention (both the denoising and the causal
+    split choice, which list-schedules the dispatch order) stays within 512
+    key splits, sizes the workspace as whole per-split partial slabs, and
+    takes little host time even for long prompts and caches."""
+    import time
+    d = dims(B=B, C=C, L=Lk, cap=Lk + C, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=dh)
+    t0 = time.perf_counter()
+    by = L.dg_attn_workspace_bytes(d)
+    assert time.perf_counter() - t0 < 2.0
+    slab = B * C * Hq * (dh + 2) * 4
+    if by:  # no workspace when every row block fits in one split
+        ns = by // slab  # the size is rounded up to 256 bytes
+        assert ns * slab <= by < ns * slab + 256
+        assert 2 <= ns <= 512
+
+
 @pytest.mark.parametrize("C,Lc,Hq,Hkv", [(16, 32768, 32, 8), (256, 1024, 16, 8), (5, 700, 6, 2)])
 def test_attention_workspace_holds_the_split_partials(L, C, Lc, Hq, Hkv):
     """Keys this long are split over several workgroups; every split leaves
