@@ -370,7 +370,7 @@ __device__ __forceinline__ u32x4 pair_load(const char* base, uint32_t off) {
 // the stores.
 __device__ __forceinline__ int pair_lds_unit(int i, int gp) { return 16 * gp + (i ^ (4 * gp)); }
 
-template <int SLICE>
+template <int SLICE, bool PIN>
 __global__ void __launch_bounds__(256, 1)
     k_vocab_pair(const u16* __restrict__ Z, const u16* __restrict__ E, int R, int d, int V, int nrb,
                  int split_len, float* __restrict__ pS, f32x4* __restrict__ pstat,
@@ -563,10 +563,11 @@ __global__ void __launch_bounds__(256, 1)
     // steps: step (c, j) is placed after matrix-core instruction j of chunk
     // c (j = 0..3 logits, 4..5 self-conditioning), so the latency of its
     // dependent vector instructions overlaps the products in flight instead
-    // of idling the matrix core.  Within a chunk the compiler may move the
-    // steps between the products (no scheduling barrier there: pinning each
-    // step to its product measured about 2% slower); the chunks themselves
-    // stay in order.
+    // of idling the matrix core.  PIN = false lets the compiler move the steps
+    // between the products of a chunk (2-5% faster from 128 rows up); PIN =
+    // true pins each step after its product (faster for a single 64-row
+    // block, where streaming E dominates: 10-16% at 1 row).  The chunks
+    // themselves stay in order either way.
     auto stage = [&](int c, int j) {
       if (c == 2 && j == 0) {
 #pragma unroll
@@ -698,6 +699,7 @@ __global__ void __launch_bounds__(256, 1)
         else
           mfma16x32_vn(e, zf[h][c], lg[h]);
         stage(c, h);
+        if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
       }
       if (c == 0) {
         // the flags' LDS latency hides behind the products above: their
@@ -714,6 +716,7 @@ __global__ void __launch_bounds__(256, 1)
       for (int hh = 0; hh < 2; ++hh) {
         acc[hh][c] = mfma32(tra[c & 1], pf[hh], acc[hh][c]);
         stage(c, 4 + hh);
+        if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
       }
       if (c == NCH - 1) mfma_v_settle(lg);
       if (c == 1) __syncthreads();  // tile t-1's partials are in LDS; tile t-3's P is read
@@ -1046,8 +1049,12 @@ hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float*
   }
   if (p.variant == 3) {
     const dim3 pgrid((unsigned)(2 * p.nrb * p.nsplit));
-    hipLaunchKernelGGL(k_vocab_pair<256>, pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb, p.split_len, pS,
-                       pstat, xhdr, (uint64_t*)(xhdr + kPairHdrWords));
+    if (p.nrb == 1)  // at most 64 rows
+      hipLaunchKernelGGL((k_vocab_pair<256, true>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb,
+                         p.split_len, pS, pstat, xhdr, (uint64_t*)(xhdr + kPairHdrWords));
+    else
+      hipLaunchKernelGGL((k_vocab_pair<256, false>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb,
+                         p.split_len, pS, pstat, xhdr, (uint64_t*)(xhdr + kPairHdrWords));
   } else if (p.variant == 1) {
     switch (sl) {
       case 32: hipLaunchKernelGGL(k_vocab32<32>, grid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb, p.split_len, pS, pstat); break;
