@@ -167,13 +167,18 @@ int enqueue_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io,
   if ((e = dg::launch_attn(ap, Q, io->k_cache, io->v_cache, Kn, Vn, O, nullptr, scratch, s,
                            (hipEvent_t)io->ev_attn_begin, (hipEvent_t)io->ev_attn_end)) != hipSuccess)
     return hip_fail(e, "attention");
-  if ((e = dg::launch_gemm_nt(dt, R, d, Hq * dh, O, w->Wo, X, Z, s)) != hipSuccess) return hip_fail(e, "output projection");
   dg::VocabPlan vp = dg::vocab_plan(R, d, dims->V, dt);
+  // the output projection also zeroes what the vocabulary head's CU-pair
+  // kernel needs cleared (the attention's partials there are consumed by now)
+  void* xregion = nullptr;
+  const size_t xbytes = dt == DG_BF16 ? dg::vocab_exchange_region(vp, scratch, &xregion) : 0;
+  if ((e = dg::launch_gemm_nt(dt, R, d, Hq * dh, O, w->Wo, X, Z, s, xregion, xbytes)) != hipSuccess)
+    return hip_fail(e, "output projection");
   // the uniform-state renoise rides on the vocabulary head's split combine
   const dg::RenoiseArgs rn{io->tokens_out, io->mask, tau, seed, t, block, dims->C, dims->V};
   if ((e = dg::launch_vocab(vp, Z, dt == DG_BF16 ? w->E_tiled : w->E, io->max_logit, io->argmax, io->conf, io->lse, io->selfcond_out,
                             scratch, s, (hipEvent_t)io->ev_vocab_begin, (hipEvent_t)io->ev_vocab_end,
-                            mask_id >= 0 ? nullptr : &rn)) != hipSuccess)
+                            mask_id >= 0 ? nullptr : &rn, xbytes > 0)) != hipSuccess)
     return hip_fail(e, "vocab/self-conditioning/renoise");
   if (mask_id >= 0) {
     if ((e = dg::launch_unmask(R, io->argmax, io->conf, tau, mask_id, io->tokens_in, io->tokens_out, io->mask,

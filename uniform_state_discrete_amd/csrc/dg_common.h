@@ -118,7 +118,11 @@ VocabPlan vocab_plan(int rows, int d, int V, int dtype);
 hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float* max_logit,
                         int32_t* argmax, float* conf, float* lse, void* selfcond, void* ws,
                         hipStream_t s, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr,
-                        const RenoiseArgs* rn = nullptr);
+                        const RenoiseArgs* rn = nullptr, bool exchange_cleared = false);
+// The region of ws that the CU-pair kernel needs zeroed before it runs
+// (tickets, flags and exchange records): its bytes (a multiple of 16), 0 for
+// the other variants.  launch_vocab clears it itself unless exchange_cleared.
+size_t vocab_exchange_region(const VocabPlan& p, void* ws, void** region);
 
 struct AttnPlan {
   int B, C, L, cap, Hq, Hkv, dh, dtype, causal, nrb, nsplit, keys_per_split;
@@ -142,8 +146,11 @@ struct GemmSeg {
   u16* C;
   int N, tiles;
 };
+// bf16: zero_bytes (a multiple of 16) at zero are also cleared by the same
+// launch, for a kernel later on the stream.
 hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const void* B,
-                          const void* Res, void* C, hipStream_t s);
+                          const void* Res, void* C, hipStream_t s, void* zero = nullptr,
+                          size_t zero_bytes = 0);
 // Q, K and V projections of the same activations in one launch (bf16), or
 // three launches (fp32).
 hipError_t launch_gemm_qkv(int dtype, int M, int K, const void* A, const void* Wq, int Nq, void* Q,

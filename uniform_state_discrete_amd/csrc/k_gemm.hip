@@ -20,7 +20,14 @@ namespace dg {
 constexpr int GKS = 64, GLD = GKS + 8;  // K slice; LDS row of 144 bytes: conflict-free
 
 __global__ void __launch_bounds__(256) k_gemm_nt_bf16(int M, int K, const u16* __restrict__ A, GemmSeg s0,
-                                                      GemmSeg s1, GemmSeg s2) {
+                                                      GemmSeg s1, GemmSeg s2, u32x4* __restrict__ zp,
+                                                      size_t zn16) {
+  if (zp) {
+    // a region a later kernel needs zeroed, spread over every thread of the grid
+    const size_t nth = (size_t)gridDim.x * gridDim.y * blockDim.x;
+    for (size_t i = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; i < zn16; i += nth)
+      zp[i] = u32x4{0u, 0u, 0u, 0u};
+  }
   __shared__ __attribute__((aligned(16))) u16 As[2][64][GLD];
   __shared__ __attribute__((aligned(16))) u16 Bs[2][64][GLD];
   int tile = blockIdx.x;
@@ -158,12 +165,13 @@ static GemmSeg gemm_seg(const void* B, const void* Res, void* C, int N) {
 }
 
 hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const void* B,
-                          const void* Res, void* C, hipStream_t s) {
+                          const void* Res, void* C, hipStream_t s, void* zero, size_t zero_bytes) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (dtype == 1) {
     const GemmSeg s0 = gemm_seg(B, Res, C, N), none = GemmSeg{nullptr, nullptr, nullptr, 0, 0};
     dim3 grid((unsigned)s0.tiles, (M + 63) / 64);
-    hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, s0, none, none);
+    hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, s0, none, none, (u32x4*)zero,
+                       zero_bytes / 16);
   } else {
     dim3 grid((N + 15) / 16, (M + 15) / 16);
     hipLaunchKernelGGL(k_gemm_nt_f32, grid, dim3(256), 0, s, M, N, K, (const float*)A,
@@ -184,7 +192,7 @@ hipError_t launch_gemm_qkv(int dtype, int M, int K, const void* A, const void* W
   const GemmSeg sq = gemm_seg(Wq, nullptr, Q, Nq), sk = gemm_seg(Wk, nullptr, Kn, Nkv),
                 sv = gemm_seg(Wv, nullptr, Vn, Nkv);
   dim3 grid((unsigned)(sq.tiles + sk.tiles + sv.tiles), (M + 63) / 64);
-  hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, sq, sk, sv);
+  hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, sq, sk, sv, nullptr, (size_t)0);
   return hipGetLastError();
 }
 

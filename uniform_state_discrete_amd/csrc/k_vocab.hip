@@ -1014,9 +1014,17 @@ VocabPlan vocab_plan(int rows, int d, int V, int dtype) {
   return p;
 }
 
+size_t vocab_exchange_region(const VocabPlan& p, void* ws, void** region) {
+  *region = nullptr;
+  if (p.rows <= 0 || p.variant != 3) return 0;
+  *region = (void*)(((uintptr_t)ws + p.part_S_bytes + p.part_stat_bytes + 255) & ~(uintptr_t)255);
+  return kPairHdrWords * 4 + (size_t)p.nrb * p.nsplit * kPairRecBytes;
+}
+
 hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float* max_logit,
                         int32_t* argmax, float* conf, float* lse, void* selfcond, void* ws,
-                        hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, const RenoiseArgs* rn) {
+                        hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, const RenoiseArgs* rn,
+                        bool exchange_cleared) {
   if (p.rows <= 0) return hipSuccess;
   if (p.variant == 0) {
     hipLaunchKernelGGL(k_vocab_f32, dim3(p.rows), dim3(256), 0, s, p.rows, p.d, p.V,
@@ -1038,10 +1046,13 @@ hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float*
   bool launched = true;
   uint32_t* xhdr = nullptr;
   if (p.variant == 3) {
-    xhdr = (uint32_t*)(((uintptr_t)ws + p.part_S_bytes + p.part_stat_bytes + 255) & ~(uintptr_t)255);
-    const size_t xbytes = kPairHdrWords * 4 + (size_t)p.nrb * p.nsplit * kPairRecBytes;
-    hipLaunchKernelGGL(k_vocab_pair_clear, dim3(512), dim3(256), 0, s, (u32x4*)xhdr, xbytes / 16);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    void* region = nullptr;
+    const size_t xbytes = vocab_exchange_region(p, ws, &region);
+    xhdr = (uint32_t*)region;
+    if (!exchange_cleared) {
+      hipLaunchKernelGGL(k_vocab_pair_clear, dim3(512), dim3(256), 0, s, (u32x4*)xhdr, xbytes / 16);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
   }
   if (ev_begin) {
     hipError_t e = hipEventRecord(ev_begin, s);
