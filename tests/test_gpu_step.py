@@ -18,6 +18,10 @@ pytestmark = pytest.mark.gpu
 
 SMALL_BF16 = Config("test_small_bf16", 90, B=2, C=40, L=70, d=256, Hq=4, Hkv=2, dh=64, V=3000,
                     dtype="bf16", steps=3, blocks=2, tau=(0.6, 0.8))
+# 1100 rows (5 canvases of 220): the projections run the 128 x 128 tile GEMM,
+# with a ragged last row tile (1100 = 8 x 128 + 76)
+MANY_ROWS_BF16 = Config("test_many_rows_bf16", 91, B=5, C=220, L=40, d=256, Hq=4, Hkv=2, dh=64, V=3000,
+                        dtype="bf16", steps=2, blocks=1, tau=(0.6, 0.6))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -100,7 +104,8 @@ def compare_full(c, o, ref, E, tau, tag):
                   ref["x_new"], ref["mask"], ref["c"], tau, extra_excl=tie)
 
 
-@pytest.mark.parametrize("cfg", [config_by_name("tiny_c16_L32_d64_V512_f32"), SMALL_BF16, config_by_name("canvas256_L1024_d2048_V32768")], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [config_by_name("tiny_c16_L32_d64_V512_f32"), SMALL_BF16, MANY_ROWS_BF16,
+                                 config_by_name("canvas256_L1024_d2048_V32768")], ids=lambda c: c.name)
 def test_step_lockstep_every_element(cfg):
     import uniform_state_discrete_amd as dg
     say(f"step lockstep {cfg.name}")

@@ -134,6 +134,128 @@ __global__ void __launch_bounds__(256) k_gemm_nt_bf16(int M, int K, const u16* _
   }
 }
 
+// bf16 path for many rows (M >= 1024: prompt prefill, many canvases): output
+// tile 128 x 128, wave tile 64 x 64 (2 x 2 products of 32 x 32 per 16-deep K
+// step).  Per K slice a wave reads 16 KiB of LDS for 16 products, half the
+// LDS bytes per product of the 64 x 64 tile, whose waves are bound by LDS
+// reads at large M.  Same operand layout, loads and epilogue convention;
+// two slices in flight through registers.
+__global__ void __launch_bounds__(256) k_gemm_nt_bf16_t128(int M, int K, const u16* __restrict__ A, GemmSeg s0,
+                                                           GemmSeg s1, GemmSeg s2, u32x4* __restrict__ zp,
+                                                           size_t zn16) {
+  if (zp) {
+    const size_t nth = (size_t)gridDim.x * gridDim.y * blockDim.x;
+    for (size_t i = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; i < zn16; i += nth)
+      zp[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  __shared__ __attribute__((aligned(16))) u16 As[2][128][GLD];
+  __shared__ __attribute__((aligned(16))) u16 Bs[2][128][GLD];
+  int tile = blockIdx.x;
+  GemmSeg sg = s0;
+  if (tile >= s0.tiles) {
+    tile -= s0.tiles;
+    sg = s1;
+    if (tile >= s1.tiles) {
+      tile -= s1.tiles;
+      sg = s2;
+    }
+  }
+  const int N = sg.N;
+  const u16* __restrict__ B = sg.B;
+  const int m0 = blockIdx.y * 128, n0 = tile * 128;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
+  const int lr = tid >> 3, lc = (tid & 7) * 8;  // loader: rows lr + 32 j (j < 4); columns lc .. lc+7
+  const int nk = K / GKS;                       // K is a multiple of 64
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(A), (short)0,
+                                                                      (int)((size_t)M * K * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(B), (short)0,
+                                                                      (int)((size_t)N * K * 2), 0x00020000);
+  const uint32_t oa = (uint32_t)(((size_t)(m0 + lr) * K + lc) * 2), ob = (uint32_t)(((size_t)(n0 + lr) * K + lc) * 2);
+  const uint32_t row32 = (uint32_t)(32 * K * 2);
+  u32x4 ga[2][4], gb[2][4];  // [slot][row group]
+  auto gload = [&](int slot, int ks) {
+    const uint32_t k2 = (uint32_t)(ks * GKS * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ga[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, oa + j * row32 + k2, 0, 0));
+      gb[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob + j * row32 + k2, 0, 0));
+    }
+  };
+  auto lstore = [&](int slot, int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *(DG_LDS u32x4*)&As[buf][lr + 32 * j][lc] = ga[slot][j];
+      *(DG_LDS u32x4*)&Bs[buf][lr + 32 * j][lc] = gb[slot][j];
+    }
+  };
+  f32x16 acc[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};  // [m half][n half]
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  gload(0, 0);
+  gload(1, 1);
+  lstore(0, 0);
+  __syncthreads();
+  // slice ks: products from LDS buffer u (= slot u), slot u refilled with
+  // slice ks + 2, slice ks + 1 (slot u ^ 1) to the other LDS buffer
+  auto slice = [&](int u, int ks) {
+    gload(u, ks + 2);
+#pragma unroll
+    for (int kk = 0; kk < GKS / 16; ++kk) {
+      u32x4 a[2], b[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        a[q] = *(const DG_LDS u32x4*)&Bs[u][wn + 32 * q + l32][kk * 16 + 8 * h];
+        b[q] = *(const DG_LDS u32x4*)&As[u][wm + 32 * q + l32][kk * 16 + 8 * h];
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma32(a[ni], b[mi], acc[mi][ni]);
+    }
+    if (ks + 1 < nk) lstore(u ^ 1, u ^ 1);
+    __syncthreads();
+  };
+  // unrolled by 2 so that the slot indexes are constants; slices past the
+  // end are loaded (in bounds of the resource) but never stored
+  const int nfull = nk & ~1;
+  for (int ks0 = 0; ks0 < nfull; ks0 += 2) {
+    slice(0, ks0);
+    slice(1, ks0 + 1);
+  }
+  if (nfull < nk) slice(0, nfull);
+  const u16* __restrict__ Res = sg.Res;
+  u16* __restrict__ C = sg.C;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int am = m0 + wm + 32 * mi + l32;
+    if (am >= M) continue;
+    // lane holds C[am][n0 + wn + 32 ni + 8j + 4h + i], i = 0..3
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn + 32 * ni + 8 * j + 4 * h;
+        if (n >= N) continue;
+        float v[4] = {acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1], acc[mi][ni][4 * j + 2], acc[mi][ni][4 * j + 3]};
+        const size_t o = (size_t)am * N + n;
+        if (n + 4 <= N) {
+          if (Res) {
+            u32x2 r = *(const u32x2*)(Res + o);
+            v[0] += bf16_to_f32(r[0] & 0xFFFFu); v[1] += bf16_to_f32(r[0] >> 16);
+            v[2] += bf16_to_f32(r[1] & 0xFFFFu); v[3] += bf16_to_f32(r[1] >> 16);
+          }
+          u32x2 out = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *(u32x2*)(C + o) = out;
+        } else {
+          for (int i = 0; i < 4 && n + i < N; ++i) {
+            float x = v[i];
+            if (Res) x += bf16_to_f32(Res[o + i]);
+            C[o + i] = (u16)f32_to_bf16(x);
+          }
+        }
+      }
+  }
+}
+
 // fp32-storage path: classic 16x16 LDS-tiled GEMM accumulating in fp64 (one
 // rounding of the stored output), sequential over K.
 __global__ void __launch_bounds__(256) k_gemm_nt_f32(int M, int N, int K, const float* __restrict__ A,
@@ -160,18 +282,26 @@ __global__ void __launch_bounds__(256) k_gemm_nt_f32(int M, int N, int K, const 
   }
 }
 
-static GemmSeg gemm_seg(const void* B, const void* Res, void* C, int N) {
-  return GemmSeg{(const u16*)B, (const u16*)Res, (u16*)C, N, (N + 63) / 64};
+// Row count from which the 128 x 128 tile kernel runs.
+constexpr int kGemmBigM = 1024;
+
+static GemmSeg gemm_seg(const void* B, const void* Res, void* C, int N, int tn) {
+  return GemmSeg{(const u16*)B, (const u16*)Res, (u16*)C, N, (N + tn - 1) / tn};
 }
 
 hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const void* B,
                           const void* Res, void* C, hipStream_t s, void* zero, size_t zero_bytes) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (dtype == 1) {
-    const GemmSeg s0 = gemm_seg(B, Res, C, N), none = GemmSeg{nullptr, nullptr, nullptr, 0, 0};
-    dim3 grid((unsigned)s0.tiles, (M + 63) / 64);
-    hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, s0, none, none, (u32x4*)zero,
-                       zero_bytes / 16);
+    const int tn = M >= kGemmBigM ? 128 : 64;
+    const GemmSeg s0 = gemm_seg(B, Res, C, N, tn), none = GemmSeg{nullptr, nullptr, nullptr, 0, 0};
+    dim3 grid((unsigned)s0.tiles, (M + tn - 1) / tn);
+    if (tn == 128)
+      hipLaunchKernelGGL(k_gemm_nt_bf16_t128, grid, dim3(256), 0, s, M, K, (const u16*)A, s0, none, none,
+                         (u32x4*)zero, zero_bytes / 16);
+    else
+      hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, s0, none, none, (u32x4*)zero,
+                         zero_bytes / 16);
   } else {
     dim3 grid((N + 15) / 16, (M + 15) / 16);
     hipLaunchKernelGGL(k_gemm_nt_f32, grid, dim3(256), 0, s, M, N, K, (const float*)A,
@@ -189,10 +319,15 @@ hipError_t launch_gemm_qkv(int dtype, int M, int K, const void* A, const void* W
     if (e == hipSuccess) e = launch_gemm_nt(dtype, M, Nkv, K, A, Wv, nullptr, Vn, s);
     return e;
   }
-  const GemmSeg sq = gemm_seg(Wq, nullptr, Q, Nq), sk = gemm_seg(Wk, nullptr, Kn, Nkv),
-                sv = gemm_seg(Wv, nullptr, Vn, Nkv);
-  dim3 grid((unsigned)(sq.tiles + sk.tiles + sv.tiles), (M + 63) / 64);
-  hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, sq, sk, sv, nullptr, (size_t)0);
+  const int tn = M >= kGemmBigM ? 128 : 64;
+  const GemmSeg sq = gemm_seg(Wq, nullptr, Q, Nq, tn), sk = gemm_seg(Wk, nullptr, Kn, Nkv, tn),
+                sv = gemm_seg(Wv, nullptr, Vn, Nkv, tn);
+  dim3 grid((unsigned)(sq.tiles + sk.tiles + sv.tiles), (M + tn - 1) / tn);
+  if (tn == 128)
+    hipLaunchKernelGGL(k_gemm_nt_bf16_t128, grid, dim3(256), 0, s, M, K, (const u16*)A, sq, sk, sv, nullptr,
+                       (size_t)0);
+  else
+    hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, sq, sk, sv, nullptr, (size_t)0);
   return hipGetLastError();
 }
 
