@@ -104,59 +104,53 @@ def attention_row(q, b, g, i, Kc, Vc, Kn, Vn, L, causal):
 
 # -- vocabulary head, confidence and self-conditioning ----------------------------
 
-def vocab_selfcond(Z, E, dtype=None, chunk=16384):
+def vocab_selfcond(Z, E, dtype=None, rows=256):
     """Full-vocabulary softmax of the tied head l = Z . E^T, per row:
 
       m   = max_v l_v                  a = lowest v attaining m
       lse = m + ln sum_v exp(l_v - m)  c = exp(m - lse)  (max probability)
       S   = sum_v P_v E_v with P = exp(l - lse)
+      gap = m - max_{v != a} l_v       (top-2 logit gap; +inf when V = 1)
 
-    Confidence is the largest probability of the row (reading of "se la
-    probabilita di un token scende al di sotto di una soglia", "Diffusione
-    dello stato uniforme": the confidence of the position's prediction).
-    S is the probability matrix times the embedding table
-    ("Autocondizionamento").  Two plain passes over the vocabulary in chunks:
-    the first finds m and a, the second sums exp(l - m) and exp(l - m) E_v.
-    Z [R, d], E [V, d] -> m, a, lse, c [R] and S [R, d] (rounded to dtype when
-    given).
+    The confidence compared with the threshold is read as the largest
+    probability of the row, i.e. how sure the model is of its own prediction
+    ("Diffusione dello stato uniforme").  S is the probability matrix times
+    the embedding table ("Autocondizionamento").  For each block of `rows`
+    rows the whole logits row is formed once and every statistic is read
+    from it directly.  The gap is not part of the method: the parity tests
+    use it to recognise near-ties of the argmax.
+    Z [R, d], E [V, d] -> m, a, lse, c, gap [R] and S [R, d] (S rounded to
+    dtype when given).
     """
     R = Z.shape[0]
     V = E.shape[0]
-    m = np.full(R, -np.inf)
-    a = np.zeros(R, np.int64)
-    for v0 in range(0, V, chunk):
-        lg = Z @ E[v0:v0 + chunk].T
-        cm = lg.max(axis=1)
-        ca = lg.argmax(axis=1) + v0          # first index among equal maxima
-        better = cm > m                      # earlier chunk wins a tie
-        a = np.where(better, ca, a)
-        m = np.where(better, cm, m)
-    l = np.zeros(R)
-    St = np.zeros((R, E.shape[1]))
-    for v0 in range(0, V, chunk):
-        Ec = E[v0:v0 + chunk]
-        p = np.exp(Z @ Ec.T - m[:, None])
-        l += p.sum(axis=1)
-        St += p @ Ec
-    lse = m + np.log(l)
+    m = np.empty(R)
+    a = np.empty(R, np.int64)
+    lse = np.empty(R)
+    gap = np.empty(R)
+    S = np.empty((R, E.shape[1]))
+    for r0 in range(0, R, rows):
+        lg = Z[r0:r0 + rows] @ E.T                   # [n, V] logits
+        n = lg.shape[0]
+        idx = np.arange(n)
+        ai = lg.argmax(axis=1)                       # first index among equal maxima
+        mi = lg[idx, ai]
+        if V > 1:
+            lg[idx, ai] = -np.inf                    # the best logit of the other ids
+            gap[r0:r0 + n] = mi - lg.max(axis=1)
+            lg[idx, ai] = mi
+        else:
+            gap[r0:r0 + n] = np.inf
+        p = np.exp(lg - mi[:, None])
+        l = p.sum(axis=1)
+        m[r0:r0 + n] = mi
+        a[r0:r0 + n] = ai
+        lse[r0:r0 + n] = mi + np.log(l)
+        S[r0:r0 + n] = (p @ E) / l[:, None]
     c = np.exp(m - lse)
-    S = St / l[:, None]
     if dtype is not None:
         S = round_store(S, dtype)
-    return m, a, lse, c, S
-
-
-def vocab_rows(Z_rows, E):
-    """The same quantities for a few rows, computed from the full logits row at
-    once (used for sampled parity at full vocabulary size)."""
-    lg = Z_rows @ E.T
-    m = lg.max(axis=1)
-    a = lg.argmax(axis=1)
-    p = np.exp(lg - m[:, None])
-    l = p.sum(axis=1)
-    srt = np.sort(lg, axis=1)
-    gap = srt[:, -1] - srt[:, -2]
-    return m, a, m + np.log(l), 1.0 / l, (p @ E) / l[:, None], gap
+    return m, a, lse, c, S, gap
 
 
 # -- uniform-state renoise ---------------------------------------------------------
@@ -224,9 +218,9 @@ def forward(H, E, W, Kc, Vc, L, x, S_prev, dtype):
     Vn = linear(Xf, W["Wv"], dtype).reshape(B, C, Hkv, dh)
     O, lse_att = attention(Q, Kc, Vc, Kn, Vn, L, causal=False, dtype=dtype)
     Z = round_store(Xf + O.reshape(B * C, Hq * dh) @ W["Wo"].T, dtype)
-    m, a, lse, c, S = vocab_selfcond(Z, E, dtype)
+    m, a, lse, c, S, gap = vocab_selfcond(Z, E, dtype)
     return dict(X=X, Q=Q, Kn=Kn, Vn=Vn, O=O, lse_att=lse_att, Z=Z.reshape(B, C, d),
-                m=m, a=a, lse=lse, c=c, S=S.reshape(B, C, d))
+                m=m, a=a, lse=lse, c=c, S=S.reshape(B, C, d), gap=gap)
 
 
 def denoise_step_masked(H, E, W, Kc, Vc, L, x, S_prev, tau, mask_id, dtype):

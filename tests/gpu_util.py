@@ -101,16 +101,3 @@ def renoise_match(name, got_x, got_mask, ref_x, ref_mask, ref_c, tau, extra_excl
         f"excluded {int(band.sum())} of {got_x.size}, renoised {int(ref_mask.sum())}")
     assert not bad_m.any() and not bad_x.any(), f"{name}: renoise mismatch"
     return int(band.sum())
-
-
-def top2_gap(Z, E, chunk=16384):
-    """oracle-side top-2 logit gap per row (float64), for the near-tie exclusion"""
-    R = Z.shape[0]
-    best = np.full((R, 2), -np.inf)
-    for v0 in range(0, E.shape[0], chunk):
-        lg = Z @ E[v0:v0 + chunk].T
-        k = min(2, lg.shape[1])
-        part = -np.sort(-lg, axis=1)[:, :k]
-        both = np.concatenate([best, part], axis=1)
-        best = -np.sort(-both, axis=1)[:, :2]
-    return best[:, 0] - best[:, 1]

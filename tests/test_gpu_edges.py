@@ -34,7 +34,7 @@ def test_vocab_single_id(R, d, dtype):
     Ef = as_f64(E, dtype)
     assert np.all(c == 1.0) and np.all(a == 0)
     assert np.array_equal(S, np.repeat(Ef[:1], R, axis=0))
-    rm, _, rlse, _, _ = step.vocab_selfcond(as_f64(Z, dtype), Ef, dtype)
+    rm, _, rlse, *_ = step.vocab_selfcond(as_f64(Z, dtype), Ef, dtype)
     close("m", m, rm, ATOL[dtype])
     close("lse", lse, rlse, ATOL[dtype])
 
@@ -45,7 +45,7 @@ def test_vocab_tiny_ragged_vocabulary(R, d, V):
     E, Z = _vocab_inputs(R, d, V, "bf16", seed=R * V + d)
     m, a, c, lse, S = _run_vocab(R, d, V, E, Z, "bf16")
     Ef, Zf = as_f64(E, "bf16"), as_f64(Z, "bf16")
-    rm, ra, rlse, rc, rS = step.vocab_selfcond(Zf, Ef, "bf16")
+    rm, ra, rlse, rc, rS, _ = step.vocab_selfcond(Zf, Ef, "bf16")
     close("m", m, rm, ATOL["bf16"])
     close("c", c, rc, ATOL["bf16"])
     close("lse", lse, rlse, ATOL["bf16"])

@@ -9,7 +9,7 @@ import torch
 
 from oracle import numerics, philox, step
 from tests.gpu_util import (ATOL, RELF, argmax_match, as_f64, close, dev, f64, need_gpu,
-                            renoise_match, say, stored, top2_gap)
+                            renoise_match, say, stored)
 
 pytestmark = pytest.mark.gpu
 
@@ -115,37 +115,34 @@ def test_vocab_matches_oracle(R, d, V, dtype):
     E, Z = _vocab_inputs(R, d, V, dtype, seed=R + d + V)
     m, a, c, lse, S = _run_vocab(R, d, V, E, Z, dtype)
     Ef, Zf = as_f64(E, dtype), as_f64(Z, dtype)
-    rm, ra, rlse, rc, rS = step.vocab_selfcond(Zf, Ef, dtype)
+    rm, ra, rlse, rc, rS, gap = step.vocab_selfcond(Zf, Ef, dtype)
     tol, rel = ATOL[dtype], RELF[dtype]
     close("m", m, rm, tol)
     close("lse", lse, rlse, tol)
     close("c", c, rc, tol)
     close("S", S, rS, tol, rel)
-    argmax_match("argmax", a, ra, top2_gap(Zf, Ef), rm)
+    argmax_match("argmax", a, ra, gap, rm)
     if R >= 16:
         assert 0.1 < rc.mean() < 0.95   # the inputs exercise a non-trivial softmax
 
 
 @pytest.mark.parametrize("d,V,rows", [(2048, 262144, 256), (4096, 262144, 256), (2048, 262144, 2048),
                                       (2048, 262144, 8), (2048, 262144, 1)])  # one 64-row CU-pair block
-def test_vocab_full_vocab_sampled_rows(d, V, rows):
-    say(f"vocab full-size d={d} V={V} R={rows} (sampled rows)")
+def test_vocab_full_vocab_every_row(d, V, rows):
+    """The full 262144-id table at the workloads' widths, every row against
+    the oracle (which forms each row's whole logits row)."""
+    say(f"vocab full-size d={d} V={V} R={rows} (every row)")
     E, Z = _vocab_inputs(rows, d, V, "bf16", seed=d + rows)
     m, a, c, lse, S = _run_vocab(rows, d, V, E, Z, "bf16")
     Ef, Zf = as_f64(E, "bf16"), as_f64(Z, "bf16")
-    idx = np.array([0, 1, 31, 32, 63, 64, 100, 127, 128, 200, 254, 255])
-    if rows > 256:
-        idx = np.concatenate([idx, [rows // 2 - 1, rows // 2, rows - 65, rows - 64, rows - 2, rows - 1]])
-    idx = idx[idx < rows]
-    rm, ra, rlse, rc, rS, gap = step.vocab_rows(Zf[idx], Ef)
-    close("m", m[idx], rm, ATOL["bf16"])
-    close("lse", lse[idx], rlse, ATOL["bf16"])
-    close("c", c[idx], rc, ATOL["bf16"])
-    close("S", S[idx], numerics.round_bf16(rS), ATOL["bf16"], RELF["bf16"])
-    argmax_match("argmax", a[idx], ra, gap, rm)
-    # properties at every row: 1/V <= c <= 1, lse >= m, finite S
+    del E
+    rm, ra, rlse, rc, rS, gap = step.vocab_selfcond(Zf, Ef, "bf16")
+    close("m", m, rm, ATOL["bf16"])
+    close("lse", lse, rlse, ATOL["bf16"])
+    close("c", c, rc, ATOL["bf16"])
+    close("S", S, rS, ATOL["bf16"], RELF["bf16"])
+    argmax_match("argmax", a, ra, gap, rm)
     assert np.all((c >= 1.0 / V * 0.999) & (c <= 1.0 + 1e-6)) and np.all(lse >= m - 1e-4)
-    assert np.all(np.isfinite(S))
 
 
 @pytest.mark.parametrize("d,dtype", [(256, "bf16"), (2048, "bf16"), (4096, "bf16"), (64, "f32")])
@@ -249,16 +246,18 @@ def test_attention_matches_oracle(B, C, L, Hq, Hkv, dh, dtype, qscale, causal):
     close("lse", lse, rlse, ATOL[dtype])
 
 
-def test_attention_long_cache_sampled_rows():
-    """The 32k-token cache, 32/8-head shape (K/V ~ N(0,1)), sampled rows."""
+def test_attention_long_cache_every_row():
+    """The 32k-token cache, 32/8-head shape (K/V ~ N(0,1)), every row."""
     B, C, L, Hq, Hkv, dh = 1, 256, 32768, 32, 8, 128
-    say("attention long cache sampled rows")
+    say("attention long cache, every row")
     arrs = _attn_inputs(B, C, L, L, Hq, Hkv, dh, "bf16", seed=7, qscale=1.0)
     O, lse = _run_attn(B, C, L, L, Hq, Hkv, dh, "bf16", arrs, 0)
     q, Kc, Vc, Kn, Vn = (as_f64(x, "bf16") for x in arrs)
+    rO, rlse = step.attention(q, Kc, Vc, Kn, Vn, L, causal=False, dtype="bf16")
+    close("O", O, rO, ATOL["bf16"], RELF["bf16"])
+    close("lse", lse, rlse, ATOL["bf16"])
+    # a few rows also through the one-query form
     G = Hq // Hkv
-    for (i, h) in [(0, 0), (1, 5), (100, 31), (255, 17), (128, 8), (37, 3)]:
+    for (i, h) in [(0, 0), (255, 17), (128, 8)]:
         ro, rl = step.attention_row(q[0, i, h], 0, h // G, i, Kc, Vc, Kn, Vn, L, False)
-        close(f"O[{i},{h}]", O[0, i, h], numerics.round_bf16(ro), ATOL["bf16"])
-        close(f"lse[{i},{h}]", lse[0, i, h], rl, ATOL["bf16"])
-    assert np.all(np.isfinite(O))
+        close(f"O[{i},{h}] one query", O[0, i, h], numerics.round_bf16(ro), ATOL["bf16"])

@@ -8,7 +8,7 @@ import torch
 
 from oracle import step
 from synth import config_by_name, Config, gen_problem
-from tests.gpu_util import ATOL, RELF, TAU_BAND, argmax_match, as_f64, close, f64, need_gpu, say, top2_gap
+from tests.gpu_util import ATOL, RELF, TAU_BAND, argmax_match, as_f64, close, f64, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -55,8 +55,17 @@ def tiny(cfg, name, idx, tau):
                   (tau, tau))
 
 
+def full_vocab(steps):
+    """The full-vocabulary workload (V = 262144, 8192-row cache) with tau 0.8
+    and the given number of steps."""
+    c = config_by_name("canvas256_L8192_d2048_V262144")
+    return Config("masked_v262144", c.index, c.B, c.C, c.L, c.d, c.Hq, c.Hkv, c.dh, c.V, c.dtype, steps, 1,
+                  (0.8, 0.8))
+
+
 @pytest.mark.parametrize("cfg", [tiny(config_by_name("tiny_c16_L32_d64_V512_f32"), "masked_tiny", 95, 0.3), SMALL_BF16,
-                                 tiny(config_by_name("canvas256_L1024_d2048_V32768"), "masked_v32768", 96, 0.9)], ids=lambda c: c.name)
+                                 tiny(config_by_name("canvas256_L1024_d2048_V32768"), "masked_v32768", 96, 0.9),
+                                 full_vocab(2)], ids=lambda c: c.name)
 def test_masked_step_lockstep(cfg):
     import uniform_state_discrete_amd as dg
     say(f"masked step lockstep {cfg.name}")
@@ -95,7 +104,7 @@ def test_masked_step_lockstep(cfg):
         close(f"{tag} c", f64(io["conf"]), ref["c"], ATOL[cfg.dtype])
         close(f"{tag} S", f64(io["selfcond_out"]).reshape(R, -1), ref["S"].reshape(R, -1), ATOL[cfg.dtype],
               RELF[cfg.dtype], bf16_ulp=cfg.dtype == "bf16")
-        gap = top2_gap(ref["Z"].reshape(R, -1), E)
+        gap = ref["gap"]
         argmax_match(f"{tag} argmax", io["argmax"].cpu().numpy(), ref["a"], gap, ref["m"])
         tie = gap < 1e-3 * np.maximum(1.0, np.abs(ref["m"]))
         band = (np.abs(ref["c"] - float(np.float32(cfg.tau[0]))) < TAU_BAND) | tie
@@ -112,44 +121,3 @@ def test_masked_step_lockstep(cfg):
         masked.append(int((got_x == mask_id).sum()))
     say(f"masked positions per step: {masked}")
     assert all(b <= a for a, b in zip(masked, masked[1:]))
-
-
-def test_masked_step_full_vocab_properties():
-    """The full-vocabulary workload (V = 262144): from a fully masked canvas,
-    every commit is a masked row whose own confidence met tau, it takes the
-    row's argmax, and committed rows stay locked on the next step."""
-    import uniform_state_discrete_amd as dg
-    c = config_by_name("canvas256_L8192_d2048_V262144")
-    say(f"masked step full vocab {c.name}")
-    p = gen_problem(c)
-    Wd = {k: dg.to_device(v) for k, v in p.W.items()}
-    Wd["E"] = dg.to_device(p.E)
-    Wd["E_tiled"] = dg.tiled_embedding(Wd["E"])
-    del p.E
-    dims = dg.make_dims(c.B, c.C, c.L, c.cap, c.d, c.Hq, c.Hkv, c.dh, c.V, dg.DG_BF16)
-    ws = dg.workspace(dg.dg_workspace_bytes(dims))
-    R = c.R
-    mask_id = 0
-    x = torch.empty((c.B, c.C), dtype=torch.int32, device="cuda")
-    dg.dg_init_masked(R, mask_id, x)
-    H, Kc, Vc = dg.to_device(p.H[0]), dg.to_device(p.Kc), dg.to_device(p.Vc)
-    S = None
-    for s in range(2):
-        io = dict(H=H, k_cache=Kc, v_cache=Vc, tokens_in=x, selfcond_in=S, tokens_out=torch.empty_like(x),
-                  selfcond_out=torch.empty((c.B, c.C, c.d), dtype=torch.bfloat16, device="cuda"),
-                  max_logit=torch.empty(R, device="cuda"), conf=torch.empty(R, device="cuda"),
-                  argmax=torch.empty(R, dtype=torch.int32, device="cuda"),
-                  mask=torch.empty(R, dtype=torch.uint8, device="cuda"))
-        dg.dg_denoise_step_masked(dims, Wd, io, 0.8, mask_id, ws)
-        torch.cuda.synchronize()
-        xi = x.cpu().numpy().reshape(-1)
-        xo = io["tokens_out"].cpu().numpy().reshape(-1)
-        k = io["mask"].cpu().numpy().astype(bool)
-        cf = io["conf"].cpu().numpy()
-        am = io["argmax"].cpu().numpy()
-        want = (xi == mask_id) & (cf >= np.float32(0.8)) & (am != mask_id)
-        assert np.array_equal(k, want)
-        assert np.array_equal(xo, np.where(want, am, xi))
-        assert np.all(np.isfinite(io["selfcond_out"].float().cpu().numpy()))
-        say(f"step {s}: {int(k.sum())} committed, {int((xo == mask_id).sum())} still masked")
-        x, S = io["tokens_out"], io["selfcond_out"]

@@ -182,6 +182,23 @@ def test_attention_permutations():
     assert np.allclose(O3, O[:, pq], atol=1e-12)
 
 
+@pytest.mark.parametrize("L,Hq,Hkv,causal", [(0, 2, 2, False), (0, 4, 1, True), (5, 3, 1, False),
+                                             (5, 4, 2, True), (5, 4, 4, False), (0, 4, 2, False)])
+def test_attention_row_matches_attention(L, Hq, Hkv, causal):
+    """attention_row (one query against its KV head) equals the batched
+    attention on every canvas, head and position, with the lse."""
+    B, C = 2, 6
+    Q, Kc, Vc, Kn, Vn = _attn_inputs(B=B, C=C, L=L, Hq=Hq, Hkv=Hkv, seed=20 + L + Hq, scale=1.5)
+    O, lse = step.attention(Q, Kc, Vc, Kn, Vn, L, causal=causal)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(C):
+                o, l = step.attention_row(Q[b, i, h], b, h // G, i, Kc, Vc, Kn, Vn, L, causal)
+                assert np.allclose(o, O[b, i, h], atol=1e-13, rtol=0)
+                assert abs(l - lse[b, i, h]) < 1e-12
+
+
 # ---- vocabulary head, confidence, self-conditioning -------------------------------------------
 
 def _emb(V=300, d=16, seed=0):
@@ -191,7 +208,7 @@ def _emb(V=300, d=16, seed=0):
 def test_vocab_matches_full_softmax_and_logsumexp():
     E = _emb()
     Z = np.random.default_rng(1).standard_normal((9, 16)) * 3
-    m, a, lse, c, S = step.vocab_selfcond(Z, E, chunk=64)            # chunked path
+    m, a, lse, c, S, gap = step.vocab_selfcond(Z, E, rows=4)            # several row blocks
     lg = Z @ E.T
     P = scipy.special.softmax(lg, axis=1)
     assert np.array_equal(a, lg.argmax(1))
@@ -200,16 +217,44 @@ def test_vocab_matches_full_softmax_and_logsumexp():
     assert np.allclose(c, P.max(1), atol=1e-14)
     assert np.allclose(S, P @ E, atol=1e-13)
     assert np.all((c >= 1.0 / E.shape[0]) & (c <= 1.0))
-    r = step.vocab_rows(Z[:3], E)
-    for u, w in zip(r[:5], (m, a, lse, c, S)):
-        assert np.allclose(u, w[:3], atol=1e-12)
+    # one row at a time gives the same rows
+    for r in (0, 4, 8):
+        u = step.vocab_selfcond(Z[r:r + 1], E)
+        for x, w in zip(u, (m, a, lse, c, S, gap)):
+            assert np.allclose(x[0], w[r], atol=1e-12)
+
+
+def _fsum_logits(Z, E):
+    """Logits by scalar loops with exactly rounded sums (math.fsum)."""
+    return [[math.fsum(z * e for z, e in zip(zr, er)) for er in E] for zr in Z]
+
+
+def test_vocab_top2_gap_brute_force():
+    E = _emb(V=97, d=8, seed=5)
+    Z = np.random.default_rng(6).standard_normal((7, 8)) * 2
+    *_, gap = step.vocab_selfcond(Z, E, rows=3)
+    for r, row in enumerate(_fsum_logits(Z.tolist(), E.tolist())):
+        top = sorted(row, reverse=True)
+        assert abs(gap[r] - (top[0] - top[1])) < 1e-12
+    # a planted near-tie: two ids whose logits differ by exactly 2^-20 in every row
+    E2 = np.zeros((6, 2))
+    E2[:, 0] = [0.1, 0.5, 0.25, 0.5 - 2.0 ** -20, -1.0, 0.0]
+    m, a, lse, c, S, gap2 = step.vocab_selfcond(np.array([[1.0, 0.0], [1.0, 3.0]]), E2)
+    assert np.array_equal(a, [1, 1]) and np.all(gap2 == 2.0 ** -20)
+    # exact ties: the gap is 0 and the lowest id wins
+    E3 = np.array([[0.0], [2.0], [1.0], [2.0]])
+    m, a, *_, gap3 = step.vocab_selfcond(np.array([[1.0]]), E3)
+    assert a[0] == 1 and gap3[0] == 0.0
+    # a single id has no runner-up
+    *_, gap4 = step.vocab_selfcond(np.array([[1.0, 2.0]]), np.array([[0.5, 0.5]]))
+    assert gap4[0] == np.inf
 
 
 def test_vocab_rows_sum_to_one_via_ones_column():
     E = _emb(V=257)
     E[:, 5] = 1.0                                                       # S[:,5] = sum_v P_v = 1
     Z = np.random.default_rng(2).standard_normal((6, 16))
-    *_, S = step.vocab_selfcond(Z, E, chunk=100)
+    S = step.vocab_selfcond(Z, E, rows=4)[4]
     assert np.allclose(S[:, 5], 1.0, atol=1e-14)
 
 
@@ -217,7 +262,7 @@ def test_vocab_one_hot_is_embedding_lookup():
     E = np.round(_emb(V=512, d=32) * 64) / 64
     y = np.array([3, 100, 511, 0])
     Z = 1000.0 * E[y]
-    m, a, lse, c, S = step.vocab_selfcond(Z, E, dtype="bf16", chunk=128)
+    m, a, lse, c, S, gap = step.vocab_selfcond(Z, E, dtype="bf16", rows=3)
     assert np.array_equal(a, y)
     assert np.all(c == 1.0)
     assert np.array_equal(S, numerics.round_bf16(E[y]))
@@ -226,17 +271,18 @@ def test_vocab_one_hot_is_embedding_lookup():
 def test_vocab_zero_input_closed_form():
     E = _emb(V=1024, d=8)
     Z = np.zeros((3, 8))
-    m, a, lse, c, S = step.vocab_selfcond(Z, E, chunk=300)
+    m, a, lse, c, S, gap = step.vocab_selfcond(Z, E, rows=2)
     assert np.all(a == 0) and np.all(m == 0)                           # ties -> lowest index
+    assert np.all(gap == 0)
     assert np.allclose(c, 1.0 / 1024, rtol=1e-15)
     assert np.allclose(lse, math.log(1024), rtol=1e-15)
     assert np.allclose(S, E.mean(0)[None], atol=1e-15)
 
 
-def test_vocab_ties_take_lowest_index_across_chunks():
+def test_vocab_ties_take_lowest_index():
     E = np.zeros((10, 2))
     E[:, 0] = [0, 1, 3, 2, 3, 1, 3, 0, 0, 0]
-    m, a, *_ = step.vocab_selfcond(np.array([[1.0, 0.0]]), E, chunk=3)
+    m, a, *_ = step.vocab_selfcond(np.array([[1.0, 0.0]]), E)
     assert a[0] == 2 and m[0] == 3.0
 
 
