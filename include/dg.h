@@ -134,6 +134,26 @@ int dg_attn_bidir(const dg_dims *dims, const void *q, const void *k_cache, const
                   const void *k_new, const void *v_new, void *out, float *lse_out, int causal,
                   void *ws, size_t ws_bytes, void *stream);
 
+/* dg_attn_bidir for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels, with the split partials kept in a
+ * scratch array built into the library instead of a caller workspace.  The
+ * call allocates nothing and frees nothing; the caller still passes the
+ * inputs and outputs.  Each GPU the library runs on holds one copy of the
+ * array (DG_ATTN_NOALLOC_MAX_BYTES, 64 MiB) from the first call on
+ * that device until the process ends.  A shape whose partials need more
+ * (dg_attn_workspace_bytes(dims) larger than that) returns DG_EWORKSPACE
+ * and enqueues nothing; the single-canvas 256-token denoising shapes with up
+ * to 32 query heads and the 16-query long-cache shape fit.  All calls on one
+ * GPU share its array: calls that may overlap in time on one GPU (different
+ * streams, or different host threads) race on it and must be serialised by
+ * the caller; consecutive calls on one stream are safe.  Arguments and
+ * errors as for dg_attn_bidir. */
+#define DG_ATTN_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+int dg_attn_bidir_noalloc(const dg_dims *dims, const void *q, const void *k_cache, const void *v_cache,
+                          const void *k_new, const void *v_new, void *out, float *lse_out, int causal,
+                          void *stream);
+
 /* Tiled layout of a bf16 embedding table for the vocabulary head.  E[V][d]
  * (row-major) is cut into blocks of 16 ids x 32 columns; block (vb, c) is
  * 1 KiB at byte offset (vb * (d / 32) + c) * 1024, and inside it entry

@@ -79,6 +79,7 @@ def lib():
             "dg_denoise_step": (ctypes.c_int, [pd, ctypes.POINTER(Weights), ctypes.POINTER(StepIO),
                                                f32, u64, u32, u32, vp, sz, vp]),
             "dg_attn_bidir": (ctypes.c_int, [pd, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]),
+            "dg_attn_bidir_noalloc": (ctypes.c_int, [pd, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp]),
             "dg_vocab_selfcond": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                                  vp, sz, vp]),
             "dg_renoise": (ctypes.c_int, [i32, i32, i32, vp, vp, f32, u64, u32, u32, vp, vp, vp]),
@@ -231,6 +232,17 @@ def dg_attn_bidir(dims, q, k_cache, v_cache, k_new, v_new, out, lse_out, causal,
                              ptr(v_new), ptr(out), ptr(lse_out, torch.float32), int(bool(causal)),
                              ptr(ws), ws.numel() if ws is not None else 0, stream_handle(stream))
     _check(st, "dg_attn_bidir")
+
+
+# DG_ATTN_NOALLOC_MAX_BYTES of include/dg.h: the built-in scratch of dg_attn_bidir_noalloc
+ATTN_NOALLOC_MAX_BYTES = 64 << 20
+
+
+def dg_attn_bidir_noalloc(dims, q, k_cache, v_cache, k_new, v_new, out, lse_out, causal, stream=None):
+    st = lib().dg_attn_bidir_noalloc(ctypes.byref(dims), ptr(q), ptr(k_cache), ptr(v_cache), ptr(k_new),
+                                     ptr(v_new), ptr(out), ptr(lse_out, torch.float32), int(bool(causal)),
+                                     stream_handle(stream))
+    _check(st, "dg_attn_bidir_noalloc")
 
 
 def dg_vocab_selfcond(rows, d, V, z, E, max_logit, argmax, conf, lse, selfcond, ws, stream=None):

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 namespace {
@@ -312,6 +313,47 @@ int enqueue_block_loop(const dg_dims* dims, const dg_weights* w, const dg_block_
   return DG_OK;
 }
 
+int check_attn(const dg_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+               const void* k_new, const void* v_new, const void* out) {
+  int st = check_dims(dims, false);
+  if (st != DG_OK) return st;
+  if (!q || !k_new || !v_new || !out || (dims->L > 0 && (!k_cache || !v_cache)))
+    return fail(DG_EINVAL, "q, k_new, v_new, out (and the caches when L > 0) must be non-NULL");
+  const void* ptrs[] = {q, k_cache, v_cache, k_new, v_new, out};
+  return check_bf16_align(dims, ptrs, 6);
+}
+
+// Device scratch of dg_attn_bidir_noalloc: the split partials of the
+// attention live in this file-scope array instead of a caller workspace, so
+// that entry point allocates nothing.  Every GPU the library runs on holds
+// its own copy until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): the
+// device address of the copy on each device is looked up once, with that
+// device current, and kept in g_scratch.
+constexpr size_t kNoAllocScratchBytes = DG_ATTN_NOALLOC_MAX_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DG_EUNSUPPORTED, "device ordinal %d is out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(DG_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return DG_OK;
+}
+
 }  // namespace
 
 struct dg_graph_s {
@@ -405,12 +447,8 @@ int dg_vocab_selfcond(int32_t rows, int32_t d, int32_t V, int32_t dtype, const v
 int dg_attn_bidir(const dg_dims* dims, const void* q, const void* k_cache, const void* v_cache,
                   const void* k_new, const void* v_new, void* out, float* lse_out, int causal,
                   void* ws, size_t ws_bytes, void* stream) {
-  int st = check_dims(dims, false);
+  int st = check_attn(dims, q, k_cache, v_cache, k_new, v_new, out);
   if (st != DG_OK) return st;
-  if (!q || !k_new || !v_new || !out || (dims->L > 0 && (!k_cache || !v_cache)))
-    return fail(DG_EINVAL, "q, k_new, v_new, out (and the caches when L > 0) must be non-NULL");
-  const void* ptrs[] = {q, k_cache, v_cache, k_new, v_new, out};
-  if ((st = check_bf16_align(dims, ptrs, 6)) != DG_OK) return st;
   const size_t need = attn_ws(dims, causal ? 1 : 0);
   if (need && (!ws || ws_bytes < need))
     return fail(DG_EWORKSPACE, "attention workspace needs %zu bytes (got %zu)", need, ws ? ws_bytes : 0);
@@ -418,6 +456,23 @@ int dg_attn_bidir(const dg_dims* dims, const void* q, const void* k_cache, const
                                  dims->head_dim, dims->dtype, causal ? 1 : 0);
   hipError_t e = dg::launch_attn(p, q, k_cache, v_cache, k_new, v_new, out, lse_out, ws, (hipStream_t)stream);
   return e == hipSuccess ? DG_OK : hip_fail(e, "dg_attn_bidir");
+}
+
+int dg_attn_bidir_noalloc(const dg_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                          const void* k_new, const void* v_new, void* out, float* lse_out, int causal,
+                          void* stream) {
+  int st = check_attn(dims, q, k_cache, v_cache, k_new, v_new, out);
+  if (st != DG_OK) return st;
+  const size_t need = attn_ws(dims, causal ? 1 : 0);
+  if (need > kNoAllocScratchBytes)
+    return fail(DG_EWORKSPACE, "this shape needs %zu bytes of split partials; the built-in scratch holds %zu",
+                need, kNoAllocScratchBytes);
+  void* sc = nullptr;
+  if (need && (st = scratch_of_current_device(&sc)) != DG_OK) return st;
+  dg::AttnPlan p = dg::attn_plan(dims->B, dims->C, dims->L, dims->cap, dims->n_q_heads, dims->n_kv_heads,
+                                 dims->head_dim, dims->dtype, causal ? 1 : 0);
+  hipError_t e = dg::launch_attn(p, q, k_cache, v_cache, k_new, v_new, out, lse_out, sc, (hipStream_t)stream);
+  return e == hipSuccess ? DG_OK : hip_fail(e, "dg_attn_bidir_noalloc");
 }
 
 int dg_denoise_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io, float tau,
