@@ -281,6 +281,20 @@ int dg_graph_capture_block_loop(const dg_dims *dims, const dg_weights *w, const 
 int dg_graph_launch(dg_graph graph, void *stream);
 void dg_graph_destroy(dg_graph graph);
 
+/* Test hook of the vocabulary head at d = 2048 and 4096 on a 256-CU device.
+ * There the head runs each 64-row block on a group of d/1024 workgroups that
+ * exchange partial logits, which needs every member of a group resident at
+ * the same time; a member that waits more than `polls` polls for the others
+ * at the start makes its group compute alone ("solo": each member computes
+ * the others' partial logits itself, with the same bits as a paired run).
+ * This sets the bound for later launches of the calling process (< 0
+ * restores the default); 0 makes every group run solo.  Results are the same
+ * either way; only the speed differs.  If a resident member stops answering
+ * in the middle of a launch (its exchange poll times out), the statistics and
+ * S of every row are NaN and argmax is -1, and each row's token is drawn as
+ * for a renoised position, so tokens stay within [0, V). */
+void dg_test_set_group_wait(int32_t polls);
+
 /* Text of a dg_status; text of the last failure on the calling thread. */
 const char *dg_status_str(int status);
 const char *dg_last_error(void);

@@ -145,6 +145,35 @@ def test_vocab_full_vocab_every_row(d, V, rows):
     assert np.all((c >= 1.0 / V * 0.999) & (c <= 1.0 + 1e-6)) and np.all(lse >= m - 1e-4)
 
 
+@pytest.mark.parametrize("R,d,V", [(100, 2048, 5000), (1, 2048, 200), (130, 2048, 7001), (37, 4096, 3000),
+                                   (256, 2048, 262144), (256, 4096, 262144)])
+def test_vocab_group_solo_equals_paired(R, d, V):
+    """The CU-group vocabulary head computing solo (each member computes the
+    other members' partial logits itself) gives the same bits as the paired
+    run: with the handshake bound 0 every group runs solo, with a bound of 1
+    some groups pair and some do not.  The small shapes are also checked
+    against the oracle."""
+    import uniform_state_discrete_amd as dg
+    say(f"vocab solo vs paired R={R} d={d} V={V}")
+    E, Z = _vocab_inputs(R, d, V, "bf16", seed=R + d + V + 1)
+    ref = _run_vocab(R, d, V, E, Z, "bf16")
+    try:
+        for polls in (0, 1):
+            dg.dg_test_set_group_wait(polls)
+            got = _run_vocab(R, d, V, E, Z, "bf16")
+            for name, u, w in zip(("m", "a", "c", "lse", "S"), got, ref):
+                assert np.array_equal(u, w), f"bound {polls}: {name} differs from the paired run"
+    finally:
+        dg.dg_test_set_group_wait(-1)
+    if V <= 8000:
+        Ef, Zf = as_f64(E, "bf16"), as_f64(Z, "bf16")
+        rm, ra, rlse, rc, rS, gap = step.vocab_selfcond(Zf, Ef, "bf16")
+        close("m", got[0], rm, ATOL["bf16"])
+        close("c", got[2], rc, ATOL["bf16"])
+        close("S", got[4], rS, ATOL["bf16"], RELF["bf16"])
+        argmax_match("argmax", got[1], ra, gap, rm)
+
+
 @pytest.mark.parametrize("d,dtype", [(256, "bf16"), (2048, "bf16"), (4096, "bf16"), (64, "f32")])
 def test_vocab_one_hot_is_exact_embedding_lookup(d, dtype):
     V, R = 3000, 40

@@ -72,3 +72,77 @@ def test_unshifted_generation_breaks():
         acc = simulate(8, seed, offset=0, cap=20000)
         broken += acc is None or any(got != tile for tile, got in acc)
     assert broken > 0
+
+
+# ---- the start handshake of a CU group ------------------------------------------------------
+
+SOLO = 1 << 8
+
+
+def handshake(Q, arrive, spin, seed):
+    """Plain-Python model of the group handshake: member m becomes runnable at
+    step arrive[m] (None: never, within the run) and then runs
+      v = fetch_or(word, bit m); loop: decided if SOLO set or all Q bits set;
+      after `spin` polls try CAS(word, v, v | SOLO), on failure re-read;
+    one atomic operation of one member per step, members picked at random.
+    A bound of 0 sets the member's bit and the solo mark at once.
+    Returns each member's decision (True = solo; None if never arrived)."""
+    rng = random.Random(seed)
+    full = (1 << Q) - 1
+    word = 0
+    state = [None] * Q        # None: not started; else dict
+    decision = [None] * Q
+    for step in range(100000):
+        ready = [m for m in range(Q) if arrive[m] is not None and arrive[m] <= step and decision[m] is None]
+        if not ready:
+            if all(decision[m] is not None or arrive[m] is None for m in range(Q)):
+                break
+            continue
+        m = rng.choice(ready)
+        st = state[m]
+        if st is None:
+            old = word
+            word |= (1 << m) | (SOLO if spin == 0 else 0)
+            state[m] = st = {"v": word if spin == 0 else old | (1 << m), "n": 0}
+        v = st["v"]
+        if (v & SOLO) or (v & full) == full:
+            decision[m] = bool(v & SOLO)
+            continue
+        if st["n"] >= spin:
+            if word == v:                      # compare-and-swap
+                word = v | SOLO
+                st["v"] = word
+            else:
+                st["v"] = word
+            continue
+        st["v"] = word                         # a poll
+        st["n"] += 1
+    return decision, word
+
+
+def test_group_handshake_members_agree():
+    for Q in (2, 4):
+        for seed in range(400):
+            rng = random.Random(seed)
+            arrive = [rng.choice([0, rng.randrange(0, 60), rng.randrange(0, 400)]) for _ in range(Q)]
+            spin = rng.choice([0, 1, 3, 20, 200])
+            dec, word = handshake(Q, arrive, spin, seed)
+            assert None not in dec, (Q, seed)
+            assert len(set(dec)) == 1, (Q, seed, dec, arrive, spin)   # one decision per group
+            if not dec[0]:
+                assert word == (1 << Q) - 1                            # paired: everyone arrived, no mark
+
+
+def test_group_handshake_pairs_when_members_arrive_together():
+    for Q in (2, 4):
+        for seed in range(50):
+            dec, _ = handshake(Q, [0] * Q, 10 ** 6, seed)
+            assert dec == [False] * Q
+
+
+def test_group_handshake_goes_solo_without_a_partner():
+    # the last member arrives only after the others have given up waiting
+    for Q in (2, 4):
+        for seed in range(50):
+            dec, word = handshake(Q, [0] * (Q - 1) + [10 ** 4], 5, seed)
+            assert dec == [True] * Q and word & SOLO

@@ -14,6 +14,6 @@ from ._lib import (  # noqa: F401
     dg_prefill_append, dg_tiled_embedding_bytes, dg_pack_embedding, tiled_embedding,
     WEIGHT_FIELDS, BlockIO, BLOCK_IO_FIELDS, Graph, dg_block_loop, dg_graph_capture_block_loop,
     dg_unmask, dg_init_masked, dg_denoise_step_masked,
-    dg_attn_bidir_noalloc, ATTN_NOALLOC_MAX_BYTES,
+    dg_attn_bidir_noalloc, ATTN_NOALLOC_MAX_BYTES, dg_test_set_group_wait,
 )
 from .device import to_device, torch_dtype  # noqa: F401

@@ -97,6 +97,7 @@ def lib():
             "dg_init_masked": (ctypes.c_int, [i32, i32, vp, vp]),
             "dg_denoise_step_masked": (ctypes.c_int, [pd, ctypes.POINTER(Weights), ctypes.POINTER(StepIO),
                                                       f32, i32, vp, sz, vp]),
+            "dg_test_set_group_wait": (None, [i32]),
             "dg_status_str": (ctypes.c_char_p, [ctypes.c_int]),
             "dg_last_error": (ctypes.c_char_p, []),
         }
@@ -243,6 +244,12 @@ def dg_attn_bidir_noalloc(dims, q, k_cache, v_cache, k_new, v_new, out, lse_out,
                                      ptr(v_new), ptr(out), ptr(lse_out, torch.float32), int(bool(causal)),
                                      stream_handle(stream))
     _check(st, "dg_attn_bidir_noalloc")
+
+
+def dg_test_set_group_wait(polls):
+    """Test hook: the start-handshake poll bound of the CU-group vocabulary
+    head (0: every group computes solo; negative: the default)."""
+    lib().dg_test_set_group_wait(int(polls))
 
 
 def dg_vocab_selfcond(rows, d, V, z, E, max_logit, argmax, conf, lse, selfcond, ws, stream=None):

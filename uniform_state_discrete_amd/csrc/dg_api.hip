@@ -375,6 +375,8 @@ const char* dg_status_str(int status) {
 
 const char* dg_last_error(void) { return g_err; }
 
+void dg_test_set_group_wait(int32_t polls) { dg::set_group_wait(polls); }
+
 size_t dg_workspace_bytes(const dg_dims* dims) {
   if (check_dims(dims, true) != DG_OK) return 0;
   return step_layout(dims).total;

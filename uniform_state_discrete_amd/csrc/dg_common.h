@@ -106,11 +106,14 @@ __device__ __forceinline__ void renoise_row(const RenoiseArgs& rn, int r, int32_
 // the hipError_t of its launch.  Pointers and sizes are already validated.
 namespace dg {
 struct VocabPlan {
-  // variant: 0 fp32 rowwise, 1 bf16 32-row, 2 bf16 16-row, 3 bf16 64-row CU pairs
-  int rows, d, V, nrb, nsplit, split_len, variant;
-  size_t part_S_bytes, part_stat_bytes, part_X_bytes;  // X: pair exchange (variant 3)
+  // variant: 0 fp32 rowwise, 1 bf16 32-row, 2 bf16 16-row, 3 bf16 64-row CU
+  // groups of `group` workgroups (2 for d = 2048, 4 for d = 4096)
+  int rows, d, V, nrb, nsplit, split_len, variant, group;
+  size_t part_S_bytes, part_stat_bytes, part_X_bytes;  // X: group exchange (variant 3)
 };
 VocabPlan vocab_plan(int rows, int d, int V, int dtype);
+// Poll bound of the CU-group handshake of later launches (< 0: the default).
+void set_group_wait(int32_t polls);
 // ev_begin / ev_end (may be NULL) are recorded around the main kernel only.
 // rn (may be NULL): the uniform-state renoise of every row, done by the split
 // combine from the row's own argmax and confidence (a separate launch on the
@@ -119,8 +122,8 @@ hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float*
                         int32_t* argmax, float* conf, float* lse, void* selfcond, void* ws,
                         hipStream_t s, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr,
                         const RenoiseArgs* rn = nullptr, bool exchange_cleared = false);
-// The region of ws that the CU-pair kernel needs zeroed before it runs
-// (tickets, flags and exchange records): its bytes (a multiple of 16), 0 for
+// The region of ws that the CU-group kernel needs zeroed before it runs
+// (tickets, flags, group words and exchange records): its bytes (a multiple of 16), 0 for
 // the other variants.  launch_vocab clears it itself unless exchange_cleared.
 size_t vocab_exchange_region(const VocabPlan& p, void* ws, void** region);
 

@@ -5,6 +5,8 @@
 // over the embedding table E that never stores the rows x V probabilities.
 #include "vocab_common.h"
 
+#include <atomic>
+
 namespace dg {
 
 // ---------------------------------------------------------------------------
@@ -294,41 +296,56 @@ __global__ void __launch_bounds__(256, 1)
 }
 
 // ---------------------------------------------------------------------------
-// Variant 64p (d = 8*SLICE): two workgroups on one XCD share 64 rows.  With
-// 32 rows per workgroup every E byte feeds too little matrix-core work: one
-// 64-cycle chunk needs 4 KiB of E from L2 and 8 KiB of LDS traffic per CU,
-// more than either path delivers.  Here a workgroup owns 64 rows and one half
-// of the columns of S = P.E (so its accumulators still fit the AGPR file):
-// per 16-id tile it reads only its half of E (32 KiB) for 2x the rows.  The
-// logits need the full-width contraction, so the two halves swap their
-// partial logits through the XCD's L2: each writes its 64 x 16 partial as
-// 64-bit words {value, tile tag} and polls the other's until all tags match
-// (no ordering between stores is needed; both sum in the same order, so both
-// compute bit-identical softmax results).  Every poll loop is bounded: on
-// timeout it raises an error flag (the combine then writes NaN) and stops
-// waiting, so no wave can hang.
+// Variant 64g (d = Q * 1024, Q = 2 or 4): a group of Q workgroups on one XCD
+// shares 64 rows.  With 32 rows per workgroup every E byte feeds too little
+// matrix-core work: one 64-cycle chunk needs 4 KiB of E from L2 and 8 KiB of
+// LDS traffic per CU, more than either path delivers.  Here a workgroup (a
+// member of the group) owns 64 rows and 1024 of the columns of S = P.E (so
+// its accumulators still fit the AGPR file): per 16-id tile it reads only its
+// 1024 columns of E (32 KiB) for 2x the rows.  The logits need the full-width
+// contraction, so the members swap their partial logits through the XCD's
+// L2: each writes its 64 x 16 partial as tagged records and polls the
+// others' until all tags match (no ordering between stores is needed; every
+// member adds the Q partials in member order, so all compute bit-identical
+// softmax results).  Every poll loop is bounded: on timeout it raises an
+// error flag (the combine then writes NaN statistics) and stops waiting, so
+// no wave can hang.
 //
-// Pairing: workgroup = 4 waves, one per SIMD, one per CU (LDS).  A workgroup
+// Grouping: workgroup = 4 waves, one per SIMD, one per CU (LDS).  A workgroup
 // reads its XCD id from the hardware and takes a ticket from that XCD's
-// counter; tickets 2k and 2k+1 on XCD x form pair x * (grid/16) + k (half =
-// ticket & 1), so partners always share an L2 whatever the dispatch order.
-// The counters and tags are cleared by k_vocab_pair_clear before each launch.
+// counter; tickets Qk .. Qk+Q-1 on XCD x form group x * (grid/8/Q) + k
+// (member = ticket % Q), so members always share an L2 whatever the dispatch
+// order.  The exchange needs every member of a group resident at once, which
+// another kernel on the GPU can prevent; so the members first agree, through
+// one word per group, whether the group runs paired or solo: each sets its
+// bit; a member that finds every bit set runs paired; one that waits longer
+// than a bound for the others marks the group solo (compare-and-swap on the
+// same word, so the decision is the same for every member).  A solo member
+// computes the other members' partial logits itself, with the same products
+// in the same order, and produces the same bits as a paired run.
+// The counters, tags and group words are cleared before each launch.
 //
-// Pipeline (iteration t, 8 chunks of 32 columns per wave):
+// Pipeline of the paired run (iteration t, 8 chunks of 32 columns per wave):
 //   logits of tile t            all chunks (E streamed through registers)
 //   partial of tile t-1         LDS exchange of the 4 waves, summed, stored
-//   softmax of tile t-2         after the other half's partial arrived
+//   softmax of tile t-2         after the other members' partials arrived
 //   P.E of tile t-3             from the 4-deep LDS ring of E tiles
 // Barriers sit at chunk boundaries where the LDS operations before them were
 // issued a full chunk of matrix-core work earlier.
 // ---------------------------------------------------------------------------
 constexpr int kPairSlots = 4;                // exchange ring depth, in tiles
 constexpr uint32_t kPairSpin = 1u << 20;     // poll bound of one exchange
+constexpr uint32_t kGroupSpin = 1u << 14;    // poll bound of the start handshake
 // header words: 0-7 tickets per XCD, 8 error flag, 9 exchange waits that
 // had to poll, 10 poll timeouts, 11 workgroups without a ticket, 12-15 the
-// first timeout (pair, iteration, half | wave << 4, lane 0's generation bit)
-constexpr int kPairHdrWords = 64;            // 256 bytes
-constexpr size_t kPairRecBytes = 2 * kPairSlots * 256 * 16;  // per pair
+// first timeout (group, iteration, member | wave << 4, lane 0's generation
+// bit), 16 solo members; words kGroupWord + g: the handshake word of group g
+constexpr int kGroupWord = 64;
+constexpr int kMaxGroups = 128;
+constexpr int kPairHdrWords = kGroupWord + kMaxGroups;   // 768 bytes
+constexpr uint32_t kGroupSolo = 1u << 8;
+// exchange records of one member: kPairSlots slots of 256 lanes x 16 bytes
+constexpr size_t kMemberRecBytes = (size_t)kPairSlots * 256 * 16;
 
 // Exchange record of a lane: its 4 partial logits, each fp32 carrying the
 // slot generation of its tile in its lowest mantissa bit.  A slot is reused
@@ -336,13 +353,13 @@ constexpr size_t kPairRecBytes = 2 * kPairSlots * 256 * 16;  // per pair
 // bit tells the wanted tile from the one before it.  The first generation has
 // bit 1, so a slot that still holds the launch's cleared zeros never matches.
 // Each 4-byte word is single-copy atomic, so a reader accepts the record once
-// all four bits match.  The bit moves a partial by at most one ulp, and both
-// halves add the same tagged values in the same order.  The partners share an
-// XCD: the store (through a buffer resource: no 64-bit lane address) reaches
-// that XCD's L2, the vector L1 being write-through; the load is a device-scope
-// global load, which misses the L1.  (A device-scope buffer load kept
-// returning the L1's stale line on gfx950, in a ping-pong probe between paired
-// workgroups.)
+// all four bits match.  The bit moves a partial by at most one ulp, and every
+// member adds the same tagged values in the same order.  The members share
+// an XCD: the store (through a buffer resource: no 64-bit lane address)
+// reaches that XCD's L2, the vector L1 being write-through; the load is a
+// device-scope global load, which misses the L1.  (A device-scope buffer load
+// kept returning the L1's stale line on gfx950, in a ping-pong probe between
+// paired workgroups.)
 __device__ __forceinline__ uint32_t pair_gen(int tile) { return (uint32_t)((tile >> 2) + 1) & 1u; }
 __device__ __forceinline__ f32x4 pair_tagged(f32x4 v, uint32_t gen) {
   f32x4 o;
@@ -370,13 +387,43 @@ __device__ __forceinline__ u32x4 pair_load(const char* base, uint32_t off) {
 // the stores.
 __device__ __forceinline__ int pair_lds_unit(int i, int gp) { return 16 * gp + (i ^ (4 * gp)); }
 
-template <int SLICE, bool PIN>
+// The start handshake of a group (thread 0 of each member): returns true when
+// the group runs solo.  Every member's decision is read from the same word:
+// paired iff all Q arrival bits were set before the solo mark.
+// A bound of 0 marks the group solo at once (every member, deterministically).
+template <int Q>
+__device__ __forceinline__ bool group_handshake(uint32_t* word, int member, uint32_t spin) {
+  const uint32_t full = (1u << Q) - 1u, mine = 1u << member;
+  if (spin == 0) {
+    __hip_atomic_fetch_or(word, mine | kGroupSolo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  }
+  uint32_t v = __hip_atomic_fetch_or(word, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) | mine;
+  for (uint32_t n = 0;; ++n) {
+    if ((v & kGroupSolo) || (v & full) == full) break;
+    if (n >= spin) {
+      // mark the group solo unless the word changed since it was read
+      uint32_t expect = v;
+      if (__hip_atomic_compare_exchange_strong(word, &expect, v | kGroupSolo, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        v |= kGroupSolo;
+        break;
+      }
+      v = expect;  // another member arrived meanwhile: decide again
+      continue;
+    }
+    v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return (v & kGroupSolo) != 0;
+}
+
+template <int Q, bool PIN>
 __global__ void __launch_bounds__(256, 1)
-    k_vocab_pair(const u16* __restrict__ Z, const u16* __restrict__ E, int R, int d, int V, int nrb,
-                 int split_len, float* __restrict__ pS, f32x4* __restrict__ pstat,
-                 uint32_t* __restrict__ xhdr, uint64_t* __restrict__ xrec) {
-  constexpr int NCH = SLICE / 32;
-  static_assert(NCH == 8, "the stage schedule assumes 8 chunks per tile");
+    k_vocab_group(const u16* __restrict__ Z, const u16* __restrict__ E, int R, int d, int V, int nrb,
+                  int split_len, float* __restrict__ pS, f32x4* __restrict__ pstat,
+                  uint32_t* __restrict__ xhdr, uint64_t* __restrict__ xrec, uint32_t group_spin) {
+  constexpr int SLICE = 256, NCH = SLICE / 32;
+  static_assert(Q == 2 || Q == 4, "groups of 2 or 4 workgroups");
   // [tile & 3][wave][chunk]: 1 KiB per chunk of 16 ids x 32 columns in 16-byte
   // units (pair_lds_unit), no padding
   __shared__ __attribute__((aligned(16))) u16 Et[4][4][NCH][512];
@@ -384,28 +431,32 @@ __global__ void __launch_bounds__(256, 1)
   __shared__ __attribute__((aligned(16))) u32x4 Pbuf[2][64];        // P of row m, ids 8k..8k+7
   __shared__ float Sbuf[64];                                        // per-row fold factor
   __shared__ __attribute__((aligned(16))) int flags[4];
-  __shared__ __attribute__((aligned(16))) f32x4 ownb[256];          // this half's partial, owner lane
-  __shared__ int role[2];
+  __shared__ __attribute__((aligned(16))) f32x4 ownb[256];          // this member's partial, owner lane
+  __shared__ int role[3];
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, r = l & 15;
   const int h2 = l >> 5, m32 = l & 31;
   if (threadIdx.x == 0) {
     const uint32_t xcc = __builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xFu;  // HW_REG_XCC_ID
     const uint32_t quota = gridDim.x / 8;
-    int pr = -1, half = 0;
+    int grp = -1, mb = 0, solo = 0;
     if (xcc < 8) {
       const uint32_t tk = __hip_atomic_fetch_add(&xhdr[xcc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (tk < quota) {
-        pr = (int)(xcc * (quota / 2) + tk / 2);
-        half = (int)(tk & 1);
+        grp = (int)(xcc * (quota / Q) + tk / Q);
+        mb = (int)(tk % Q);
       }
     }
-    if (pr < 0) {
+    if (grp < 0) {
       __hip_atomic_store(&xhdr[8], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_add(&xhdr[11], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      solo = group_handshake<Q>(&xhdr[kGroupWord + grp], mb, group_spin) ? 1 : 0;
+      if (solo) __hip_atomic_fetch_add(&xhdr[16], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    role[0] = pr;
-    role[1] = half;
+    role[0] = grp;
+    role[1] = mb;
+    role[2] = solo;
   }
   const u32x4 z4 = {0u, 0u, 0u, 0u};
   for (int e = threadIdx.x; e < 2 * 64; e += 256) (&Pbuf[0][0])[e] = z4;
@@ -418,22 +469,15 @@ __global__ void __launch_bounds__(256, 1)
     }
   }
   __syncthreads();
-  const int pair = __builtin_amdgcn_readfirstlane(role[0]), hf = __builtin_amdgcn_readfirstlane(role[1]);
-  if (pair < 0) return;  // the whole workgroup: no ticket (error raised)
-  const int rb = pair % nrb, split = pair / nrb;
+  const int grp = __builtin_amdgcn_readfirstlane(role[0]), mb = __builtin_amdgcn_readfirstlane(role[1]);
+  const bool solo = __builtin_amdgcn_readfirstlane(role[2]) != 0;
+  if (grp < 0) return;  // the whole workgroup: no ticket (error raised)
+  const int rb = grp % nrb, split = grp / nrb;
   const int r0 = rb * 64;
   const int vs = split * split_len, ve = min(V, vs + split_len);
-  const int dbase = hf * (d >> 1) + w * SLICE;
-  const size_t tofs = (size_t)gridDim.x / 2 / nrb * R * d;  // temp area follows the nsplit partials
-
-  // Z fragments of rows 16h + r, columns dbase + 32c + 8g .. +7
-  u32x4 zf[4][NCH];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const u16* zp = Z + (size_t)min(r0 + 16 * h + r, R - 1) * d + dbase + 8 * g;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) zf[h][c] = swap_halves(ldg128(zp + 32 * c), g & 1);
-  }
+  const int dq = d / Q;  // columns per member
+  const int dbase = mb * dq + w * SLICE;
+  const size_t tofs = (size_t)gridDim.x / Q / nrb * R * d;  // temp area follows the nsplit partials
 
   const int nt = ve > vs ? (ve - vs + 15) / 16 : 0;
   // the 4 row blocks that stream one split start at different tiles of each
@@ -458,12 +502,6 @@ __global__ void __launch_bounds__(256, 1)
   const uint32_t blk_row = (uint32_t)d * 32u;
   const __amdgpu_buffer_rsrc_t erc = buffer_rsrc(E, (uint32_t)(((size_t)V + 15) / 16 * blk_row));
   const uint32_t lane_off = (uint32_t)((size_t)(vs / 16) * blk_row + (size_t)(dbase / 32) * 1024u + l * 16u);
-  u32x4 ring[NCH];
-  auto issue = [&](int c, int step) {
-    ring[c] = buffer_ld128(erc, lane_off + (uint32_t)phys(step) * blk_row + 1024u * c);
-  };
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) issue(c, 0);
 
   u32x4 tra[2];
   auto tr_load = [&](const DG_LDS u16* tile, int c, int slot) {
@@ -471,8 +509,6 @@ __global__ void __launch_bounds__(256, 1)
     const u32x2 b = lds_read_tr16(tile + tr_off[1] + 512 * c);
     tra[slot] = u32x4{a[0], a[1], b[0], b[1]};
   };
-  tr_load((const DG_LDS u16*)&Et[1][w][0][0], 0, 0);  // tile -3: zeros
-  tr_load((const DG_LDS u16*)&Et[1][w][0][0], 1, 1);
 
   // softmax owner: row 16w + rho, ids 4q .. 4q+3 (lane 4 rho + q)
   const int rho = l >> 2, q = l & 3, orow = 16 * w + rho;
@@ -480,29 +516,12 @@ __global__ void __launch_bounds__(256, 1)
   int amax = 0;
   bool g_valid = false, broken = false;
   u32x4 pf[2] = {z4, z4};
-  f32x4 lg[4];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) lg[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 own_old = {0.f, 0.f, 0.f, 0.f};
-  u32x4 xp = z4;
   const int xw = 16 * g + ((r + 4 * g) & 15);
   const int xr = 16 * q + ((rho + 4 * q) & 15);
-  // exchange records: [pair][half][slot][256 lanes][4 words]; uniform bases
-  // plus a 32-bit lane offset
-  const __amdgpu_buffer_rsrc_t xrc = buffer_rsrc(xrec, (uint32_t)(gridDim.x / 2 * kPairRecBytes));
-  const uint32_t xo_out = (uint32_t)((pair * 2 + hf) * kPairSlots) * 4096u;
-  const char* const xo_in = (const char*)xrec + (size_t)((pair * 2 + (hf ^ 1)) * kPairSlots) * 4096;
-  const uint32_t xlane = threadIdx.x * 16u;
-
-  f32x16 acc[2][NCH];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) acc[hh][c] = zero16();
 
   // G = (G + acc) s (G = acc s on the first fold; the first fold stores the
   // raw accumulator to G, a later one to the temp area T, merged after)
-  auto fold = [&](float s, bool scale) {
+  auto fold = [&](f32x16 (&acc)[2][NCH], float s, bool scale) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int zr = r0 + 32 * hh + m32;
@@ -540,97 +559,65 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
       for (int c = 0; c < NCH; ++c) acc[hh][c] = zero16();
   };
+  // after the last tile: the final fold and the row statistics (member 0)
+  auto finish = [&](f32x16 (&acc)[2][NCH]) {
+    fold(acc, 1.f, false);
+    const float tot = lsum + dpp_f<0xB1>(lsum);
+    const float tot4 = tot + dpp_f<0x4E>(tot);
+    if (mb == 0 && r0 + orow < R && q == 0)
+      pstat[(size_t)split * R + r0 + orow] = f32x4{m_seg, tot4, m_true, __int_as_float(amax)};
+  };
 
-  for (int t = 0; t <= nt + 2; ++t) {
-    // Tile t-1's partial logits and tile t-3's softmax output (written in
-    // the previous iteration) become visible.
-    __syncthreads();
-    pf[0] = Pbuf[h2][m32];
-    pf[1] = Pbuf[h2][32 + m32];
-    typedef int i32x4_t __attribute__((ext_vector_type(4)));
-    i32x4_t flv = *(const DG_LDS i32x4_t*)flags;  // combined after chunk 0's logit products
-    const bool own_ok = t >= 1 && t - 1 < nt;  // tile t-1 is exchanged
-    const bool sm_ok = t >= 2 && t - 2 < nt;   // tile t-2 gets its softmax
-    const int v2 = vs + 16 * (sm_ok ? phys(t - 2) : 0);
-    DG_LDS u16* tile = (DG_LDS u16*)&Et[t & 3][w][0][0];
-    const DG_LDS u16* tpe = (const DG_LDS u16*)&Et[(t + 1) & 3][w][0][0];   // tile t-3
-    const DG_LDS u16* tnx = (const DG_LDS u16*)&Et[(t + 2) & 3][w][0][0];   // tile t-2
-    f32x4 xa[4], own;
-    float x[4];
-    float tm = -INFINITY, s = 1.f, ms = 0.f;
-    bool over = false, first = false;
-    // The softmax of tile t-2 and the exchange of tile t-1, cut into small
-    // steps: step (c, j) is placed after matrix-core instruction j of chunk
-    // c (j = 0..3 logits, 4..5 self-conditioning), so the latency of its
-    // dependent vector instructions overlaps the products in flight instead
-    // of idling the matrix core.  PIN = false lets the compiler move the steps
-    // between the products of a chunk (2-5% faster from 128 rows up); PIN =
-    // true pins each step after its product (faster for a single 64-row
-    // block, where streaming E dominates: 10-16% at 1 row).  The chunks
-    // themselves stay in order either way.
-    auto stage = [&](int c, int j) {
-      if (c == 2 && j == 0) {
+  if (solo) {
+    f32x16 acc[2][NCH];
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) xa[s4] = xch[s4][w][xr];
-      }
-      if (c == 3 && j == 0) {
-        own_old = ownb[threadIdx.x];  // this half's partial of tile t-2, parked last iteration
-        own = xa[0] + xa[1];
-      }
-      if (c == 3 && j == 1) own = (own + xa[2]) + xa[3];
-      if (c == 3 && j == 2) {
-        own = pair_tagged(own, pair_gen(t - 1));
-        ownb[threadIdx.x] = own;
-      }
-      if (c == 3 && j == 3 && own_ok)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, own), xrc, xlane,
-                                               xo_out + ((t - 1) & 3) * 4096u, 0);
-      if (c == 4 && j == 0 && sm_ok) {
-        const uint32_t want = pair_gen(t - 2);
-        bool ok = pair_gen_ok(xp, want);
-        if (!__all(ok) && !broken) {
-          if (l == 0) __hip_atomic_fetch_add(&xhdr[9], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const char* so = xo_in + ((t - 2) & 3) * 4096;
-          for (uint32_t n = 0;; ++n) {
-            xp = pair_load(so, xlane);
-            ok = pair_gen_ok(xp, want);
-            if (__all(ok)) break;
-            if (n >= kPairSpin) {
-              broken = true;
-              if (l == 0) {
-                __hip_atomic_store(&xhdr[8], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (__hip_atomic_fetch_add(&xhdr[10], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-                  xhdr[12] = (uint32_t)pair;
-                  xhdr[13] = (uint32_t)t;
-                  xhdr[14] = (uint32_t)(hf | (w << 4));
-                  xhdr[15] = xp[0] & 1u;
-                }
-              }
-              break;
-            }
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) acc[hh][c] = zero16();
+    // ---- solo run: every member's partial computed here, then the same
+    // softmax and P.E as the paired run, one tile at a time ----
+    DG_LDS u16* tile = (DG_LDS u16*)&Et[0][w][0][0];
+    for (int s = 0; s < nt; ++s) {
+      const int ph = phys(s);
+      const int v2 = vs + 16 * ph;
+      f32x4 x4 = {0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < Q; ++m) {
+        const int cb = m * dq + w * SLICE;  // member m's columns of this wave
+        const uint32_t moff = (uint32_t)((size_t)(vs / 16) * blk_row + (size_t)(cb / 32) * 1024u + l * 16u) +
+                              (uint32_t)ph * blk_row;
+        f32x4 lg[4] = {};
+#pragma unroll 1
+        for (int c = 0; c < NCH; ++c) {
+          const u32x4 e = buffer_ld128(erc, moff + 1024u * c);
+          if (m == mb) *(DG_LDS u32x4*)(tile + wr + 512 * c) = e;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const u32x4 zf = swap_halves(ldg128(Z + (size_t)min(r0 + 16 * h + r, R - 1) * d + cb + 32 * c + 8 * g),
+                                         g & 1);
+            lg[h] = mfma16x32(e, zf, c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : lg[h]);
           }
         }
-      }
-      if (c == 4 && j == 1) {
-        // both halves add half 0's partial first
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = __uint_as_float(xp[i]);
-          x[i] = hf == 0 ? own_old[i] + pv : pv + own_old[i];
-        }
-      }
-      if (c == 4 && j == 2 && !(sm_ok && v2 + 16 <= ve)) {
-        // a ragged or absent tile (uniform): ids past the split are -inf
+        for (int h = 0; h < 4; ++h) xch[w][h][xw] = lg[h];
+        __syncthreads();
+        f32x4 xa[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = sm_ok && v2 + 4 * q + i < ve ? x[i] : -INFINITY;
+        for (int s4 = 0; s4 < 4; ++s4) xa[s4] = xch[s4][w][xr];
+        f32x4 own = xa[0] + xa[1];
+        own = (own + xa[2]) + xa[3];
+        own = pair_tagged(own, pair_gen(s));
+        x4 = m == 0 ? own : x4 + own;
+        __syncthreads();
       }
-      if (c == 4 && j == 3) tm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      if (c == 4 && j == 4) tm = fmaxf(tm, dpp_f<0xB1>(tm));
-      if (c == 4 && j == 5) tm = fmaxf(tm, dpp_f<0x4E>(tm));  // the row's tile max, in all 4 lanes
-      if (c == 5 && j == 0 && __any(tm >= m_true)) {
-        // the running max may move (uniform branch, rare after a split's
-        // first tiles): lowest id attaining the tile max; tiles come out of
-        // id order, so a tie goes to the lower id
+      float x[4] = {x4[0], x4[1], x4[2], x4[3]};
+      if (!(v2 + 16 <= ve)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = v2 + 4 * q + i < ve ? x[i] : -INFINITY;
+      }
+      float tm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      tm = fmaxf(tm, dpp_f<0xB1>(tm));
+      tm = fmaxf(tm, dpp_f<0x4E>(tm));
+      if (__any(tm >= m_true)) {
         int cand = 0x7FFFFFFF;
 #pragma unroll
         for (int i = 3; i >= 0; --i) cand = x[i] == tm ? v2 + 4 * q + i : cand;
@@ -640,103 +627,279 @@ __global__ void __launch_bounds__(256, 1)
         amax = better ? cand : amax;
         m_true = fmaxf(m_true, tm);
       }
-      if (c == 5 && j == 1) {
-        // Lazy reference: it only moves when a logit exceeds it by more than
-        // kLazyTh; the running sum is then rescaled by s = e^(m_old - m_new).
-        first = m_seg == -INFINITY;
-        over = !first & (tm > m_seg + kLazyTh);
-        s = over ? __builtin_amdgcn_exp2f((m_seg - tm) * kLog2e) : 1.f;
-      }
-      if (c == 5 && j == 2) {
-        m_seg = (first | over) ? tm : m_seg;
-        ms = m_seg == -INFINITY ? 0.f : m_seg;  // a row with no valid logit yet: all p are 0
-      }
-      // p = 2^((x - m) log2 e): exact 1 at the maximum, 0 for a masked -inf;
-      // results below 2^-126 flush to 0 (more than 87 below the reference)
-      if (c == 5 && j == 3) {
-        x[0] = __builtin_amdgcn_exp2f((x[0] - ms) * kLog2e);
-        x[1] = __builtin_amdgcn_exp2f((x[1] - ms) * kLog2e);
-      }
-      if (c == 5 && j == 4) {
-        x[2] = __builtin_amdgcn_exp2f((x[2] - ms) * kLog2e);
-        x[3] = __builtin_amdgcn_exp2f((x[3] - ms) * kLog2e);
-      }
-      if (c == 5 && j == 5) lsum = fmaf(lsum, s, (x[0] + x[1]) + (x[2] + x[3]));
-      if (c == 6 && j == 0) {
+      const bool first = m_seg == -INFINITY;
+      const bool over = !first & (tm > m_seg + kLazyTh);
+      const float sc = over ? __builtin_amdgcn_exp2f((m_seg - tm) * kLog2e) : 1.f;
+      m_seg = (first | over) ? tm : m_seg;
+      const float ms = m_seg == -INFINITY ? 0.f : m_seg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = __builtin_amdgcn_exp2f((x[i] - ms) * kLog2e);
+      lsum = fmaf(lsum, sc, (x[0] + x[1]) + (x[2] + x[3]));
+      {
         typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
         typedef float f32x2v __attribute__((ext_vector_type(2)));
         const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x[0], x[1]}, bf16x2v));
         const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x[2], x[3]}, bf16x2v));
         *(DG_LDS u32x2*)((DG_LDS char*)&Pbuf[q >> 1][orow] + 8 * (q & 1)) = u32x2{lo, hi};
       }
-      if (c == 6 && j == 1) {
-        // every lane of a row writes the same factor, every lane of the wave
-        // the same flag (no branch; orow = threadIdx.x / 4)
-        Sbuf[threadIdx.x >> 2] = s;
-        flags[__builtin_amdgcn_readfirstlane(w)] = __any(s != 1.f) ? 1 : 0;
-      }
-    };
+      Sbuf[threadIdx.x >> 2] = sc;
+      flags[__builtin_amdgcn_readfirstlane(w)] = __any(sc != 1.f) ? 1 : 0;
+      __syncthreads();
+      pf[0] = Pbuf[h2][m32];
+      pf[1] = Pbuf[h2][32 + m32];
+      if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) fold(acc, 0.f, true);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const u32x4 e = ring[c];
-      if (c == 0) {
-        // tile t-1's partial logits of this wave (finished last iteration)
+      for (int c = 0; c < NCH; ++c) {
+        tr_load(tile, c, 0);
 #pragma unroll
-        for (int h = 0; h < 4; ++h) xch[w][h][xw] = lg[h];
-      }
-      *(DG_LDS u32x4*)(tile + wr + 512 * c) = e;
-      if (c == 7 && own_ok) {
-        // the other half's partial of tile t-1 (stored at chunk 3 of this
-        // iteration), consumed at chunk 4 of the next
-        xp = pair_load(xo_in + ((t - 1) & 3) * 4096, xlane);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        // e comes from memory, zf is constant: no VALU write precedes
-        if (c == 0)
-          mfma16x32_v0(e, zf[h][c], lg[h]);  // a new tile's chain starts from 0
-        else
-          mfma16x32_vn(e, zf[h][c], lg[h]);
-        stage(c, h);
-        if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
-      }
-      if (c == 0) {
-        // the flags' LDS latency hides behind the products above: their
-        // first use is pinned after them
-        asm volatile("" : "+v"(flv));
-        if (t >= 3 && (flv[0] | flv[1] | flv[2] | flv[3]) != 0) {
-          // tile t-3's softmax moved a reference: fold the products of the
-          // tiles before it under the old one
-          fold(0.f, true);
-        }
+        for (int hh = 0; hh < 2; ++hh) acc[hh][c] = mfma32(tra[0], pf[hh], acc[hh][c]);
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        acc[hh][c] = mfma32(tra[c & 1], pf[hh], acc[hh][c]);
-        stage(c, 4 + hh);
-        if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
-      }
-      if (c == NCH - 1) mfma_v_settle(lg);
-      if (c == 1) __syncthreads();  // tile t-1's partials are in LDS; tile t-3's P is read
-      // A operand of chunk c+2 of tile t-3 (slot c & 1 was just consumed), or
-      // of chunks 0, 1 of tile t-2 for the next iteration
-      if (c + 2 < NCH)
-        tr_load(tpe, c + 2, c & 1);
-      else
-        tr_load(tnx, c + 2 - NCH, c & 1);
-      // chunk c of tile t+1 into the slot this chunk's products just read
-      issue(c, t + 1);
-      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();  // the tile, P and the flags are rewritten next tile
     }
+    finish(acc);
+    return;
   }
-  fold(1.f, false);
+  {
+    // ---- paired run ----
+    f32x16 acc[2][NCH];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) acc[hh][c] = zero16();
+    // Z fragments of rows 16h + r, columns dbase + 32c + 8g .. +7
+    u32x4 zf[4][NCH];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const u16* zp = Z + (size_t)min(r0 + 16 * h + r, R - 1) * d + dbase + 8 * g;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) zf[h][c] = swap_halves(ldg128(zp + 32 * c), g & 1);
+    }
+    u32x4 ring[NCH];
+    auto issue = [&](int c, int step) {
+      ring[c] = buffer_ld128(erc, lane_off + (uint32_t)phys(step) * blk_row + 1024u * c);
+    };
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) issue(c, 0);
+    tr_load((const DG_LDS u16*)&Et[1][w][0][0], 0, 0);  // tile -3: zeros
+    tr_load((const DG_LDS u16*)&Et[1][w][0][0], 1, 1);
 
-  const float tot = lsum + dpp_f<0xB1>(lsum);
-  const float tot4 = tot + dpp_f<0x4E>(tot);
-  if (hf == 0 && r0 + orow < R && q == 0)
-    pstat[(size_t)split * R + r0 + orow] = f32x4{m_seg, tot4, m_true, __int_as_float(amax)};
+    f32x4 lg[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) lg[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 own_old = {0.f, 0.f, 0.f, 0.f};
+    u32x4 xp[Q - 1];
+#pragma unroll
+    for (int k = 0; k < Q - 1; ++k) xp[k] = z4;
+    // exchange records: [group][member][slot][256 lanes][4 words]; uniform
+    // bases plus a 32-bit lane offset
+    const __amdgpu_buffer_rsrc_t xrc = buffer_rsrc(xrec, (uint32_t)(gridDim.x * kMemberRecBytes));
+    const uint32_t xo_out = (uint32_t)(((size_t)grp * Q + mb) * kMemberRecBytes);
+    // other member k (k < Q - 1) is member k + (k >= mb)
+    auto xo_in = [&](int k) {
+      return (const char*)xrec + ((size_t)grp * Q + k + (k >= mb ? 1 : 0)) * kMemberRecBytes;
+    };
+    const uint32_t xlane = threadIdx.x * 16u;
+
+    for (int t = 0; t <= nt + 2; ++t) {
+      // Tile t-1's partial logits and tile t-3's softmax output (written in
+      // the previous iteration) become visible.
+      __syncthreads();
+      pf[0] = Pbuf[h2][m32];
+      pf[1] = Pbuf[h2][32 + m32];
+      typedef int i32x4_t __attribute__((ext_vector_type(4)));
+      i32x4_t flv = *(const DG_LDS i32x4_t*)flags;  // combined after chunk 0's logit products
+      const bool own_ok = t >= 1 && t - 1 < nt;  // tile t-1 is exchanged
+      const bool sm_ok = t >= 2 && t - 2 < nt;   // tile t-2 gets its softmax
+      const int v2 = vs + 16 * (sm_ok ? phys(t - 2) : 0);
+      DG_LDS u16* tile = (DG_LDS u16*)&Et[t & 3][w][0][0];
+      const DG_LDS u16* tpe = (const DG_LDS u16*)&Et[(t + 1) & 3][w][0][0];   // tile t-3
+      const DG_LDS u16* tnx = (const DG_LDS u16*)&Et[(t + 2) & 3][w][0][0];   // tile t-2
+      f32x4 xa[4], own;
+      float x[4];
+      float tm = -INFINITY, s = 1.f, ms = 0.f;
+      bool over = false, first = false;
+      // The softmax of tile t-2 and the exchange of tile t-1, cut into small
+      // steps: step (c, j) is placed after matrix-core instruction j of chunk
+      // c (j = 0..3 logits, 4..5 self-conditioning), so the latency of its
+      // dependent vector instructions overlaps the products in flight instead
+      // of idling the matrix core.  PIN = false lets the compiler move the steps
+      // between the products of a chunk (2-5% faster from 128 rows up); PIN =
+      // true pins each step after its product (faster for a single 64-row
+      // block, where streaming E dominates: 10-16% at 1 row).  The chunks
+      // themselves stay in order either way.
+      auto stage = [&](int c, int j) {
+        if (c == 2 && j == 0) {
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) xa[s4] = xch[s4][w][xr];
+        }
+        if (c == 3 && j == 0) {
+          own_old = ownb[threadIdx.x];  // this member's partial of tile t-2, parked last iteration
+          own = xa[0] + xa[1];
+        }
+        if (c == 3 && j == 1) own = (own + xa[2]) + xa[3];
+        if (c == 3 && j == 2) {
+          own = pair_tagged(own, pair_gen(t - 1));
+          ownb[threadIdx.x] = own;
+        }
+        if (c == 3 && j == 3 && own_ok)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, own), xrc, xlane,
+                                                 xo_out + ((t - 1) & 3) * 4096u, 0);
+        if (c == 4 && j == 0 && sm_ok) {
+          const uint32_t want = pair_gen(t - 2);
+#pragma unroll
+          for (int k = 0; k < Q - 1; ++k) {
+            bool ok = pair_gen_ok(xp[k], want);
+            if (!__all(ok) && !broken) {
+              if (l == 0) __hip_atomic_fetch_add(&xhdr[9], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              const char* so = xo_in(k) + ((t - 2) & 3) * 4096;
+              for (uint32_t n = 0;; ++n) {
+                xp[k] = pair_load(so, xlane);
+                ok = pair_gen_ok(xp[k], want);
+                if (__all(ok)) break;
+                if (n >= kPairSpin) {
+                  broken = true;
+                  if (l == 0) {
+                    __hip_atomic_store(&xhdr[8], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (__hip_atomic_fetch_add(&xhdr[10], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+                      xhdr[12] = (uint32_t)grp;
+                      xhdr[13] = (uint32_t)t;
+                      xhdr[14] = (uint32_t)(mb | (w << 4));
+                      xhdr[15] = xp[k][0] & 1u;
+                    }
+                  }
+                  break;
+                }
+              }
+            }
+          }
+        }
+        if (c == 4 && j == 1) {
+          // every member adds the Q partials in member order
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float a = mb == 0 ? own_old[i] : __uint_as_float(xp[0][i]);
+#pragma unroll
+            for (int m = 1; m < Q; ++m)
+              a += m == mb ? own_old[i] : __uint_as_float(xp[m - (m > mb ? 1 : 0)][i]);
+            x[i] = a;
+          }
+        }
+        if (c == 4 && j == 2 && !(sm_ok && v2 + 16 <= ve)) {
+          // a ragged or absent tile (uniform): ids past the split are -inf
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = sm_ok && v2 + 4 * q + i < ve ? x[i] : -INFINITY;
+        }
+        if (c == 4 && j == 3) tm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        if (c == 4 && j == 4) tm = fmaxf(tm, dpp_f<0xB1>(tm));
+        if (c == 4 && j == 5) tm = fmaxf(tm, dpp_f<0x4E>(tm));  // the row's tile max, in all 4 lanes
+        if (c == 5 && j == 0 && __any(tm >= m_true)) {
+          // the running max may move (uniform branch, rare after a split's
+          // first tiles): lowest id attaining the tile max; tiles come out of
+          // id order, so a tie goes to the lower id
+          int cand = 0x7FFFFFFF;
+#pragma unroll
+          for (int i = 3; i >= 0; --i) cand = x[i] == tm ? v2 + 4 * q + i : cand;
+          cand = min(cand, dpp_i<0xB1>(cand));
+          cand = min(cand, dpp_i<0x4E>(cand));
+          const bool better = (tm > m_true) | ((tm == m_true) & (tm != -INFINITY) & (cand < amax));
+          amax = better ? cand : amax;
+          m_true = fmaxf(m_true, tm);
+        }
+        if (c == 5 && j == 1) {
+          // Lazy reference: it only moves when a logit exceeds it by more than
+          // kLazyTh; the running sum is then rescaled by s = e^(m_old - m_new).
+          first = m_seg == -INFINITY;
+          over = !first & (tm > m_seg + kLazyTh);
+          s = over ? __builtin_amdgcn_exp2f((m_seg - tm) * kLog2e) : 1.f;
+        }
+        if (c == 5 && j == 2) {
+          m_seg = (first | over) ? tm : m_seg;
+          ms = m_seg == -INFINITY ? 0.f : m_seg;  // a row with no valid logit yet: all p are 0
+        }
+        // p = 2^((x - m) log2 e): exact 1 at the maximum, 0 for a masked -inf;
+        // results below 2^-126 flush to 0 (more than 87 below the reference)
+        if (c == 5 && j == 3) {
+          x[0] = __builtin_amdgcn_exp2f((x[0] - ms) * kLog2e);
+          x[1] = __builtin_amdgcn_exp2f((x[1] - ms) * kLog2e);
+        }
+        if (c == 5 && j == 4) {
+          x[2] = __builtin_amdgcn_exp2f((x[2] - ms) * kLog2e);
+          x[3] = __builtin_amdgcn_exp2f((x[3] - ms) * kLog2e);
+        }
+        if (c == 5 && j == 5) lsum = fmaf(lsum, s, (x[0] + x[1]) + (x[2] + x[3]));
+        if (c == 6 && j == 0) {
+          typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+          typedef float f32x2v __attribute__((ext_vector_type(2)));
+          const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x[0], x[1]}, bf16x2v));
+          const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x[2], x[3]}, bf16x2v));
+          *(DG_LDS u32x2*)((DG_LDS char*)&Pbuf[q >> 1][orow] + 8 * (q & 1)) = u32x2{lo, hi};
+        }
+        if (c == 6 && j == 1) {
+          // every lane of a row writes the same factor, every lane of the wave
+          // the same flag (no branch; orow = threadIdx.x / 4)
+          Sbuf[threadIdx.x >> 2] = s;
+          flags[__builtin_amdgcn_readfirstlane(w)] = __any(s != 1.f) ? 1 : 0;
+        }
+      };
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const u32x4 e = ring[c];
+        if (c == 0) {
+          // tile t-1's partial logits of this wave (finished last iteration)
+#pragma unroll
+          for (int h = 0; h < 4; ++h) xch[w][h][xw] = lg[h];
+        }
+        *(DG_LDS u32x4*)(tile + wr + 512 * c) = e;
+        if (c == 7 && own_ok) {
+          // the other members' partials of tile t-1 (stored at chunk 3 of
+          // this iteration), consumed at chunk 4 of the next
+#pragma unroll
+          for (int k = 0; k < Q - 1; ++k) xp[k] = pair_load(xo_in(k) + ((t - 1) & 3) * 4096, xlane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          // e comes from memory, zf is constant: no VALU write precedes
+          if (c == 0)
+            mfma16x32_v0(e, zf[h][c], lg[h]);  // a new tile's chain starts from 0
+          else
+            mfma16x32_vn(e, zf[h][c], lg[h]);
+          stage(c, h);
+          if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
+        }
+        if (c == 0) {
+          // the flags' LDS latency hides behind the products above: their
+          // first use is pinned after them
+          asm volatile("" : "+v"(flv));
+          if (t >= 3 && (flv[0] | flv[1] | flv[2] | flv[3]) != 0) {
+            // tile t-3's softmax moved a reference: fold the products of the
+            // tiles before it under the old one
+            fold(acc, 0.f, true);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          acc[hh][c] = mfma32(tra[c & 1], pf[hh], acc[hh][c]);
+          stage(c, 4 + hh);
+          if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
+        }
+        if (c == NCH - 1) mfma_v_settle(lg);
+        if (c == 1) __syncthreads();  // tile t-1's partials are in LDS; tile t-3's P is read
+        // A operand of chunk c+2 of tile t-3 (slot c & 1 was just consumed), or
+        // of chunks 0, 1 of tile t-2 for the next iteration
+        if (c + 2 < NCH)
+          tr_load(tpe, c + 2, c & 1);
+        else
+          tr_load(tnx, c + 2 - NCH, c & 1);
+        // chunk c of tile t+1 into the slot this chunk's products just read
+        issue(c, t + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    finish(acc);
+  }
 }
 
 // Zeroes the pair tickets, error flag and exchange tags (a kernel, so that
@@ -765,13 +928,16 @@ __global__ void __launch_bounds__(256) k_vocab_combine(int R, int d, int nsplit,
   __shared__ float sh[4];
   const int r = blockIdx.x;
   if (err && *err) {
-    // a paired split lost its partner: every output of the row is NaN
+    // a resident group member stopped answering (its exchange timed out):
+    // the statistics and S of every row are NaN (argmax -1), and the row's
+    // token is drawn as for a renoised position, so the token stream stays
+    // within [0, V)
     if (threadIdx.x == 0) {
       max_logit[r] = NAN;
       argmax[r] = -1;
       conf[r] = NAN;
       if (lse) lse[r] = NAN;
-      if (rn.out) renoise_row(rn, r, -1, NAN);   // NaN is never below tau: token -1
+      if (rn.out) renoise_row(rn, r, 0, -INFINITY);
     }
     for (int e = threadIdx.x; e < d; e += 256) {
       if (out_bf16) ((u16*)S)[(size_t)r * d + e] = 0x7FC0;
@@ -956,19 +1122,24 @@ hipError_t launch_pack_embedding(int V, int d, const void* E, void* E_tiled, hip
 }
 
 // ---------------------------------------------------------------------------
-// CU pairs need all 8 XCDs of a full MI355X (256 CUs, one workgroup each).
-static bool pair_capable() {
-  static int cached[64];
-  static bool init[64];
+// CU groups need all 8 XCDs of a full MI355X (256 CUs, one workgroup each).
+static bool group_capable() {
+  static std::atomic<int> cached[64];  // 0 unknown, 1 no, 2 yes
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-  if (!init[dev]) {
+  int c = cached[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     int n = 0;
-    cached[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n == 256;
-    init[dev] = true;
+    c = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n == 256 ? 2 : 1;
+    cached[dev].store(c, std::memory_order_relaxed);
   }
-  return cached[dev] != 0;
+  return c == 2;
 }
+
+// Poll bound of the group handshake (a test hook can set it to 0, which
+// makes every group run solo).
+static std::atomic<uint32_t> g_group_spin{kGroupSpin};
+void set_group_wait(int32_t polls) { g_group_spin.store(polls < 0 ? kGroupSpin : (uint32_t)polls); }
 
 VocabPlan vocab_plan(int rows, int d, int V, int dtype) {
   VocabPlan p{};
@@ -978,11 +1149,13 @@ VocabPlan vocab_plan(int rows, int d, int V, int dtype) {
     return p;
   }
   const int vt = 16, tiles = (V + vt - 1) / vt;
-  if (d == 2048 && (rows + 63) / 64 <= 128 && pair_capable()) {
-    // CU pairs, 64 rows: 2 nrb nsplit = 256 workgroups at most, a multiple
-    // of 16 so that every XCD holds whole pairs
+  const int Q = d / 1024;
+  if ((d == 2048 || d == 4096) && group_capable()) {
+    // CU groups of Q = d / 1024 workgroups, 64 rows: Q nrb nsplit = 256
+    // workgroups at most, with nrb nsplit a multiple of 8 so that every XCD
+    // holds whole groups
     const int nrb = (rows + 63) / 64;
-    int ns = 128 / nrb;
+    int ns = 256 / Q / nrb;
     while (ns > 0 && (nrb * ns) % 8 != 0) --ns;
     if (ns > tiles) {
       ns = tiles;
@@ -990,12 +1163,13 @@ VocabPlan vocab_plan(int rows, int d, int V, int dtype) {
     }
     if (ns > 0) {
       p.variant = 3;
+      p.group = Q;
       p.nrb = nrb;
       p.split_len = (tiles + ns - 1) / ns * vt;
       p.nsplit = ns;  // trailing splits may be empty: they contribute nothing
       p.part_S_bytes = 2 * (size_t)p.nsplit * rows * d * sizeof(float);
       p.part_stat_bytes = (size_t)p.nsplit * rows * sizeof(f32x4);
-      p.part_X_bytes = 256 + kPairHdrWords * 4 + (size_t)nrb * ns * kPairRecBytes;
+      p.part_X_bytes = 256 + kPairHdrWords * 4 + (size_t)nrb * ns * Q * kMemberRecBytes;
       return p;
     }
   }
@@ -1018,7 +1192,7 @@ size_t vocab_exchange_region(const VocabPlan& p, void* ws, void** region) {
   *region = nullptr;
   if (p.rows <= 0 || p.variant != 3) return 0;
   *region = (void*)(((uintptr_t)ws + p.part_S_bytes + p.part_stat_bytes + 255) & ~(uintptr_t)255);
-  return kPairHdrWords * 4 + (size_t)p.nrb * p.nsplit * kPairRecBytes;
+  return kPairHdrWords * 4 + (size_t)p.nrb * p.nsplit * p.group * kMemberRecBytes;
 }
 
 hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float* max_logit,
@@ -1059,13 +1233,18 @@ hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float*
     if (e != hipSuccess) return e;
   }
   if (p.variant == 3) {
-    const dim3 pgrid((unsigned)(2 * p.nrb * p.nsplit));
-    if (p.nrb == 1)  // at most 64 rows
-      hipLaunchKernelGGL((k_vocab_pair<256, true>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb,
-                         p.split_len, pS, pstat, xhdr, (uint64_t*)(xhdr + kPairHdrWords));
+    const dim3 pgrid((unsigned)(p.group * p.nrb * p.nsplit));
+    uint64_t* xrec = (uint64_t*)(xhdr + kPairHdrWords);
+    const uint32_t spin = g_group_spin.load();
+    if (p.group == 4)
+      hipLaunchKernelGGL((k_vocab_group<4, false>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb,
+                         p.split_len, pS, pstat, xhdr, xrec, spin);
+    else if (p.nrb == 1)  // at most 64 rows
+      hipLaunchKernelGGL((k_vocab_group<2, true>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb,
+                         p.split_len, pS, pstat, xhdr, xrec, spin);
     else
-      hipLaunchKernelGGL((k_vocab_pair<256, false>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb,
-                         p.split_len, pS, pstat, xhdr, (uint64_t*)(xhdr + kPairHdrWords));
+      hipLaunchKernelGGL((k_vocab_group<2, false>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb,
+                         p.split_len, pS, pstat, xhdr, xrec, spin);
   } else if (p.variant == 1) {
     switch (sl) {
       case 32: hipLaunchKernelGGL(k_vocab32<32>, grid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb, p.split_len, pS, pstat); break;
