@@ -492,11 +492,10 @@ __global__ void __launch_bounds__(256, 1)
   // pairs store their upper half first).  Ids 4 apart flip bit 2 of the
   // unit's low part: the second read offset is the first with bit 5 flipped.
   const int wr = 8 * pair_lds_unit(r, g);
-  int tr_off[2];
+  int tr_off0;  // the second read is at tr_off0 ^ 32
   {
     const int p = l & 15, cg = 4 * ((l >> 4) & 1) + (p & 3), gp = cg >> 1;
-    tr_off[0] = 8 * pair_lds_unit(8 * h2 + (p >> 2), gp) + 4 * ((cg & 1) ^ (gp & 1));
-    tr_off[1] = tr_off[0] ^ 32;
+    tr_off0 = 8 * pair_lds_unit(8 * h2 + (p >> 2), gp) + 4 * ((cg & 1) ^ (gp & 1));
   }
 
   const uint32_t blk_row = (uint32_t)d * 32u;
@@ -505,8 +504,8 @@ __global__ void __launch_bounds__(256, 1)
 
   u32x4 tra[2];
   auto tr_load = [&](const DG_LDS u16* tile, int c, int slot) {
-    const u32x2 a = lds_read_tr16(tile + tr_off[0] + 512 * c);
-    const u32x2 b = lds_read_tr16(tile + tr_off[1] + 512 * c);
+    const u32x2 a = lds_read_tr16(tile + tr_off0 + 512 * c);
+    const u32x2 b = lds_read_tr16(tile + (tr_off0 ^ 32) + 512 * c);
     tra[slot] = u32x4{a[0], a[1], b[0], b[1]};
   };
 
@@ -695,9 +694,12 @@ __global__ void __launch_bounds__(256, 1)
     // bases plus a 32-bit lane offset
     const __amdgpu_buffer_rsrc_t xrc = buffer_rsrc(xrec, (uint32_t)(gridDim.x * kMemberRecBytes));
     const uint32_t xo_out = (uint32_t)(((size_t)grp * Q + mb) * kMemberRecBytes);
-    // other member k (k < Q - 1) is member k + (k >= mb)
+    // other member k (k < Q - 1) is member k + (k >= mb); its records are
+    // addressed as the uniform base plus a 32-bit offset (the region is a
+    // few MiB), so no 64-bit lane addresses stay live across the loop
+    const char* const xbase = (const char*)xrec;
     auto xo_in = [&](int k) {
-      return (const char*)xrec + ((size_t)grp * Q + k + (k >= mb ? 1 : 0)) * kMemberRecBytes;
+      return (uint32_t)(((size_t)grp * Q + k + (k >= mb ? 1 : 0)) * kMemberRecBytes);
     };
     const uint32_t xlane = threadIdx.x * 16u;
 
@@ -752,9 +754,11 @@ __global__ void __launch_bounds__(256, 1)
             bool ok = pair_gen_ok(xp[k], want);
             if (!__all(ok) && !broken) {
               if (l == 0) __hip_atomic_fetch_add(&xhdr[9], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              const char* so = xo_in(k) + ((t - 2) & 3) * 4096;
+              uint32_t xl = xlane;
+              asm volatile("" : "+v"(xl));
+              const uint32_t so = xo_in(k) + ((t - 2) & 3) * 4096u + xl;
               for (uint32_t n = 0;; ++n) {
-                xp[k] = pair_load(so, xlane);
+                xp[k] = pair_load(xbase, so);
                 ok = pair_gen_ok(xp[k], want);
                 if (__all(ok)) break;
                 if (n >= kPairSpin) {
@@ -853,9 +857,13 @@ __global__ void __launch_bounds__(256, 1)
         *(DG_LDS u32x4*)(tile + wr + 512 * c) = e;
         if (c == 7 && own_ok) {
           // the other members' partials of tile t-1 (stored at chunk 3 of
-          // this iteration), consumed at chunk 4 of the next
+          // this iteration), consumed at chunk 4 of the next; the lane offset
+          // is made opaque here, so the per-member offsets are added at each
+          // load instead of being kept live across the loop
+          uint32_t xl = xlane;
+          asm volatile("" : "+v"(xl));
 #pragma unroll
-          for (int k = 0; k < Q - 1; ++k) xp[k] = pair_load(xo_in(k) + ((t - 1) & 3) * 4096, xlane);
+          for (int k = 0; k < Q - 1; ++k) xp[k] = pair_load(xbase, xo_in(k) + ((t - 1) & 3) * 4096u + xl);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
