@@ -52,16 +52,24 @@ def algorithmic(cfg):
 
 def read_traffic(workload):
     """HBM bytes per flash-vocab launch from the committed rocprofv3 counter
-    runs, or None when they were taken on a different kernel source or
-    another workload."""
+    runs (one record per workload), or None when the record was taken on a
+    different kernel source or is missing for this workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != vocab_source_hash() or t.get("workload") != workload:
-        return None
-    return t.get("bytes_per_launch")
+    recs = t.get("records", []) if isinstance(t, dict) else []
+    h = vocab_source_hash()
+    for r in recs:
+        if r.get("workload") == workload and r.get("source_sha256") == h:
+            return r.get("bytes_per_launch")
+    return None
+
+
+def pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
 
 
 def cpu_baseline(p, cfg, min_seconds=10.0):
@@ -129,7 +137,7 @@ def attention_hbm_shape(stream, reps=20):
             "mfma_frac": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
 
 
-def block_loop_graph(stream, replays=2):
+def block_loop_graph(stream, replays=3):
     """The block-diffusion workload (8 canvases of 256 tokens over their own
     4096-row caches, 4 blocks of 32 steps with tau annealed 0.5 -> 0.95, a
     causal append after each block) captured into one HIP graph by
@@ -141,8 +149,7 @@ def block_loop_graph(stream, replays=2):
     c = config_by_name("blocks4_canvas8x256_L4096_d2048_V262144")
     p = gen_problem(c)
     W = {k: dg.to_device(v) for k, v in p.W.items()}
-    W["E"] = dg.to_device(p.E)
-    W["E_tiled"] = dg.tiled_embedding(W["E"])
+    W["E"] = dg.model_embedding(dg.to_device(p.E))
     Kc, Vc = dg.to_device(p.Kc), dg.to_device(p.Vc)
     H = torch.stack([dg.to_device(h) for h in p.H]).contiguous()
     del p
@@ -159,17 +166,20 @@ def block_loop_graph(stream, replays=2):
     g = dg.dg_graph_capture_block_loop(dims, W, io, taus, c.steps, c.blocks, c.seed, ws, stream)
     g.launch(stream)                        # warm-up replay
     stream.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    seq = []
     for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         g.launch(stream)
-    e1.record(stream)
-    stream.synchronize()
-    ms = e0.elapsed_time(e1) / replays
+        e1.record(stream)
+        stream.synchronize()
+        seq.append(e0.elapsed_time(e1))
+    ms = pct(seq, 50)
     g.close()
     n_steps = c.steps * c.blocks
     alg = algorithmic(c)
     return {"workload": c.name, "graph_replays": replays, "ms_per_sequence": round(ms, 3),
+            "ms_per_sequence_p10": round(pct(seq, 10), 3), "ms_per_sequence_p90": round(pct(seq, 90), 3),
             "sequence": f"{c.blocks} blocks x ({c.steps} denoise steps + causal append) over {c.B} canvases",
             "steps_per_s": round(n_steps / (ms * 1e-3), 2),
             "canvas_tokens_per_s": round(n_steps * R / (ms * 1e-3), 1),
@@ -285,16 +295,143 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}))
 
 
+def run_workload(cfg, steps, warmup, replays, stream, keep_problem=False):
+    """The denoise step of one workload, chained over `steps` steps (step s
+    consumes step s-1's tokens and self-conditioning vector):
+      - eager: `steps` steps between HIP events on the launch stream, with
+        the per-kernel event hooks of the attention and flash-vocab kernels;
+      - graph: the same `steps` steps captured once into a HIP graph and
+        replayed `replays` times, each replay timed with HIP events; median,
+        p10 and p90 of the time per step.
+    Inputs are generated and uploaded before any timed region."""
+    import numpy as np
+    import torch
+
+    import uniform_state_discrete_amd as dg
+    from synth import gen_problem, tau_schedule
+
+    p = gen_problem(cfg)
+    W = {k: dg.to_device(v) for k, v in p.W.items()}
+    W["E"] = dg.model_embedding(dg.to_device(p.E))   # once per model, outside any timed region
+    Kc, Vc, H = dg.to_device(p.Kc), dg.to_device(p.Vc), dg.to_device(p.H[0])
+    fdt = W["E"].dtype
+    code = dg.DG_BF16 if cfg.dtype == "bf16" else dg.DG_F32
+    dims = dg.make_dims(cfg.B, cfg.C, cfg.L, cfg.cap, cfg.d, cfg.Hq, cfg.Hkv, cfg.dh, cfg.V, code)
+    ws = dg.workspace(dg.dg_workspace_bytes(dims))
+    R = cfg.R
+    tok = [torch.empty((cfg.B, cfg.C), dtype=torch.int32, device="cuda") for _ in range(2)]
+    sc = [torch.zeros((cfg.B, cfg.C, cfg.d), dtype=fdt, device="cuda") for _ in range(2)]
+    stats = dict(max_logit=torch.empty(R, device="cuda"), conf=torch.empty(R, device="cuda"),
+                 lse=torch.empty(R, device="cuda"), argmax=torch.empty(R, dtype=torch.int32, device="cuda"),
+                 mask=torch.empty(R, dtype=torch.uint8, device="cuda"))
+    taus = tau_schedule(cfg)
+    dg.dg_init_canvas(R, cfg.C, cfg.V, cfg.seed, 0, tok[0], stream)
+
+    def mk_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)       # materialise the HIP event
+        return evs
+
+    ev = {k: mk_events(steps) for k in ("vb", "ve", "ab", "ae")}
+
+    def run(s, strm, timed_index=None):
+        a, b = s % 2, (s + 1) % 2
+        io = dict(H=H, k_cache=Kc, v_cache=Vc, tokens_in=tok[a], selfcond_in=None if s == 0 else sc[a],
+                  tokens_out=tok[b], selfcond_out=sc[b], **stats)
+        if timed_index is not None:
+            io.update(ev_vocab_begin=ev["vb"][timed_index], ev_vocab_end=ev["ve"][timed_index],
+                      ev_attn_begin=ev["ab"][timed_index], ev_attn_end=ev["ae"][timed_index])
+        dg.dg_denoise_step(dims, W, io, taus[s % cfg.steps], cfg.seed, s % cfg.steps + 1, 0, ws, strm)
+
+    with torch.cuda.stream(stream):
+        for s in range(warmup):
+            run(s, stream)
+    torch.cuda.synchronize()
+    kept = [1.0 - float(stats["mask"].float().mean())]
+    t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    t0e.record(stream)
+    for k in range(steps):
+        run(k, stream, k)
+    t1e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_eager = t0e.elapsed_time(t1e) / steps
+    kept.append(1.0 - float(stats["mask"].float().mean()))
+    vocab_ms = [ev["vb"][k].elapsed_time(ev["ve"][k]) for k in range(steps)]
+    attn_ms = [ev["ab"][k].elapsed_time(ev["ae"][k]) for k in range(steps)]
+
+    # the same steps as one HIP graph, replayed
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.graph(g, stream=cap, capture_error_mode="relaxed"):
+        for k in range(steps):
+            run(k, cap)
+    torch.cuda.synchronize()
+    g.replay()                                   # warm-up replay
+    torch.cuda.synchronize()
+    per_step = []
+    cur = torch.cuda.current_stream()
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        g.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        per_step.append(e0.elapsed_time(e1) / steps)
+    del g
+
+    alg = algorithmic(cfg)
+    v_avg = float(np.mean(vocab_ms))
+    a_avg = float(np.mean(attn_ms))
+    ms_med = pct(per_step, 50)
+    achieved = alg["fl_vocab"] / (v_avg * 1e-3) / 1e12
+    out = dict(
+        workload=cfg.name, steps=steps, warmup=warmup,
+        ms_per_step=ms_med, ms_per_step_p10=pct(per_step, 10), ms_per_step_p90=pct(per_step, 90),
+        graph_replays=replays, ms_per_step_eager=ms_eager, wall_s_timed_eager=wall,
+        steps_per_s=1000.0 / ms_med, canvas_tokens_per_s=1000.0 / ms_med * R,
+        step_mfma_frac=alg["flops"] / (ms_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        step_hbm_frac=alg["bytes"] / (ms_med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        flash_vocab_ms=v_avg, flash_vocab_ms_p10=pct(vocab_ms, 10), flash_vocab_ms_p90=pct(vocab_ms, 90),
+        attention_ms=a_avg,
+        attention_mfma_frac=alg["fl_attn"] / (a_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        attention_hbm_frac=alg["by_cache"] / (a_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        kept_fraction=kept,
+        roofline={"kernel": "flash-vocab (logits, softmax stats, P.E)", "bound": "mfma",
+                  "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": read_traffic(cfg.name),
+                  "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                  "algorithmic_bytes": alg["by_E"] + cfg.B * cfg.C * cfg.d * 2.0,
+                  "algorithmic_flops": alg["fl_vocab"]})
+    return out, (p, W, H) if keep_problem else None
+
+
+def rounded(x, nd=4):
+    if isinstance(x, float):
+        return round(x, nd)
+    if isinstance(x, dict):
+        return {k: rounded(v, nd) for k, v in x.items()}
+    if isinstance(x, list):
+        return [rounded(v, nd) for v in x]
+    return x
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--replays", type=int, default=10, help="timed graph replays of the steps")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn-hbm", action="store_true", help="skip the HBM-bound attention shape")
     ap.add_argument("--no-block-loop", action="store_true", help="skip the block-diffusion graph replay")
     ap.add_argument("--no-prefill", action="store_true", help="skip the causal prompt prefill")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the 32k-vocabulary and long-context workloads")
     ap.add_argument("--sweep-rows", action="store_true",
                     help="only run the rows sweep of the vocabulary head and attention (one JSON line per size)")
     ap.add_argument("--copy-mib", type=int, default=0, help="only run a plain copy of this size")
@@ -312,86 +449,23 @@ def main():
         crossover_sweep(torch.cuda.current_stream())
         return
 
-    import numpy as np
     import torch
 
-    import uniform_state_discrete_amd as dg
-    from synth import config_by_name, gen_problem, tau_schedule
+    from synth import config_by_name
 
     cfg = config_by_name(args.workload)
     torch.cuda.set_device(0)
-    p = gen_problem(cfg)
-    W = {k: dg.to_device(v) for k, v in p.W.items()}
-    W["E"] = dg.to_device(p.E)
-    W["E_tiled"] = dg.tiled_embedding(W["E"])   # once per model, outside any timed region
-    Kc, Vc, H = dg.to_device(p.Kc), dg.to_device(p.Vc), dg.to_device(p.H[0])
-    fdt = W["E"].dtype
-    code = dg.DG_BF16 if cfg.dtype == "bf16" else dg.DG_F32
-    dims = dg.make_dims(cfg.B, cfg.C, cfg.L, cfg.cap, cfg.d, cfg.Hq, cfg.Hkv, cfg.dh, cfg.V, code)
-    ws = dg.workspace(dg.dg_workspace_bytes(dims))
-    R = cfg.R
-    tok = [torch.empty((cfg.B, cfg.C), dtype=torch.int32, device="cuda") for _ in range(2)]
-    sc = [torch.zeros((cfg.B, cfg.C, cfg.d), dtype=fdt, device="cuda") for _ in range(2)]
-    stats = dict(max_logit=torch.empty(R, device="cuda"), conf=torch.empty(R, device="cuda"),
-                 lse=torch.empty(R, device="cuda"), argmax=torch.empty(R, dtype=torch.int32, device="cuda"),
-                 mask=torch.empty(R, dtype=torch.uint8, device="cuda"))
-    taus = tau_schedule(cfg)
     stream = torch.cuda.current_stream()
-    dg.dg_init_canvas(R, cfg.C, cfg.V, cfg.seed, 0, tok[0])
-
-    def mk_events(n):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        for e in evs:
-            e.record(stream)       # materialise the HIP event
-        return evs
-
-    K = args.steps
-    ev = {k: mk_events(K) for k in ("vb", "ve", "ab", "ae")}
-    kept = []
-
-    def run(s, timed_index=None):
-        a, b = s % 2, (s + 1) % 2
-        io = dict(H=H, k_cache=Kc, v_cache=Vc, tokens_in=tok[a], selfcond_in=None if s == 0 else sc[a],
-                  tokens_out=tok[b], selfcond_out=sc[b], **stats)
-        if timed_index is not None:
-            io.update(ev_vocab_begin=ev["vb"][timed_index], ev_vocab_end=ev["ve"][timed_index],
-                      ev_attn_begin=ev["ab"][timed_index], ev_attn_end=ev["ae"][timed_index])
-        dg.dg_denoise_step(dims, W, io, taus[s % cfg.steps], cfg.seed, s % cfg.steps + 1, 0, ws, stream)
-
-    for s in range(args.warmup):
-        run(s)
-    torch.cuda.synchronize()
-    kept.append(1.0 - float(stats["mask"].float().mean()))
-    t0e = torch.cuda.Event(enable_timing=True)
-    t1e = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    t0e.record(stream)
-    for k in range(K):
-        run(args.warmup + k, k)
-    t1e.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_total = t0e.elapsed_time(t1e)
-    ms_step = ms_total / K
-    kept.append(1.0 - float(stats["mask"].float().mean()))
-    vocab_ms = [ev["vb"][k].elapsed_time(ev["ve"][k]) for k in range(K)]
-    attn_ms = [ev["ab"][k].elapsed_time(ev["ae"][k]) for k in range(K)]
-    v_avg = float(np.mean(vocab_ms))
-    a_avg = float(np.mean(attn_ms))
-
-    alg = algorithmic(cfg)
-    achieved = alg["fl_vocab"] / (v_avg * 1e-3) / 1e12
-    traffic = read_traffic(cfg.name)
-    steps_s = 1000.0 / ms_step
+    r, keep = run_workload(cfg, args.steps, args.warmup, args.replays, stream, keep_problem=True)
+    p, W, H = keep
     out = {
         "metric": "canvas denoise steps/s (256 tok, V=262144) + % MFMA peak, % HBM peak",
-        "value": round(steps_s, 3),
+        "value": round(r["steps_per_s"], 3),
         "unit": "steps/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -400,21 +474,24 @@ def main():
         "config": {"workload": cfg.name, "canvases": cfg.B, "canvas_tokens": cfg.C, "kv_cache": cfg.L,
                    "d_model": cfg.d, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.dh,
                    "vocab": cfg.V, "tau": cfg.tau[0], "parallelism": "1 GPU"},
-        "canvas_tokens_per_s": round(steps_s * R, 1),
-        "step_mfma_frac": round(alg["flops"] / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "step_hbm_frac": round(alg["bytes"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "flash_vocab_ms": round(v_avg, 4),
-        "attention_ms": round(a_avg, 4),
-        "attention_mfma_frac": round(alg["fl_attn"] / (a_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "attention_hbm_frac": round(alg["by_cache"] / (a_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "kept_fraction": [round(k, 3) for k in kept],
-        "wall_s_timed": round(wall, 3),
-        "roofline": {"kernel": "flash-vocab (logits, softmax stats, P.E)", "bound": "mfma",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
-                     "algorithmic_bytes": alg["by_E"] + cfg.B * cfg.C * cfg.d * 2.0},
+        "timing": "median of the graph replays (each replays the chained steps); p10/p90 beside it",
     }
+    for k in ("ms_per_step_p10", "ms_per_step_p90", "graph_replays", "ms_per_step_eager", "canvas_tokens_per_s",
+              "step_mfma_frac", "step_hbm_frac", "flash_vocab_ms", "flash_vocab_ms_p10", "flash_vocab_ms_p90",
+              "attention_ms", "attention_mfma_frac", "attention_hbm_frac", "kept_fraction", "wall_s_timed_eager"):
+        out[k] = rounded(r[k])
+    out["roofline"] = rounded(r["roofline"])
+    if not args.no_other_workloads and args.workload == DEFAULT_WORKLOAD:
+        others = []
+        for name, steps in (("canvas256_L1024_d2048_V32768", 16), ("canvas256_L32768_d4096_V262144", 8)):
+            o, _ = run_workload(config_by_name(name), steps, 2, 5, stream)
+            others.append(rounded({k: o[k] for k in ("workload", "steps", "steps_per_s", "ms_per_step",
+                                                     "ms_per_step_p10", "ms_per_step_p90", "ms_per_step_eager",
+                                                     "canvas_tokens_per_s", "step_mfma_frac", "flash_vocab_ms",
+                                                     "attention_ms", "attention_mfma_frac", "attention_hbm_frac",
+                                                     "roofline")}))
+            torch.cuda.empty_cache()
+        out["other_workloads"] = others
     if not args.no_attn_hbm:
         out["attention_hbm_shape"] = attention_hbm_shape(stream)
     if not args.no_prefill:

@@ -67,13 +67,12 @@ typedef struct {
 
 /* Model tensors.  Projection weights are stored output-major, like a linear
  * layer's weight: Wq[Hq*dh][d], Wk[Hkv*dh][d], Wv[Hkv*dh][d], Wo[d][Hq*dh].
- * E[V][d] is the token-embedding table, also the tied vocabulary head.
- * E_tiled is the same table in the tiled layout of dg_pack_embedding, read by
- * the bf16 vocabulary head (the row-major E serves the token gathers);
- * required for DG_BF16, ignored for DG_F32. */
+ * E is the token-embedding table, also the tied vocabulary head: for DG_F32
+ * the row-major E[V][d]; for DG_BF16 the same table in the tiled layout of
+ * dg_pack_embedding (the only copy the bf16 path needs: the vocabulary head
+ * streams it and the token gathers read their rows from it). */
 typedef struct {
   const void *Wq, *Wk, *Wv, *Wo, *E;
-  const void *E_tiled;
 } dg_weights;
 
 /* Per-step tensors (R = B*C rows, row r = canvas r / C, position r % C). */
@@ -154,7 +153,9 @@ int dg_attn_bidir_noalloc(const dg_dims *dims, const void *q, const void *k_cach
                           const void *k_new, const void *v_new, void *out, float *lse_out, int causal,
                           void *stream);
 
-/* Tiled layout of a bf16 embedding table for the vocabulary head.  E[V][d]
+/* Tiled layout of a bf16 embedding table (the form dg_weights.E takes for
+ * DG_BF16; convert once per model, then the row-major table can be freed).
+ * E[V][d]
  * (row-major) is cut into blocks of 16 ids x 32 columns; block (vb, c) is
  * 1 KiB at byte offset (vb * (d / 32) + c) * 1024, and inside it entry
  * (id 16 vb + r, column 32 c + 8 g + e) sits at element 8 (16 g + r) + e'

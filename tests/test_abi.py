@@ -115,7 +115,6 @@ def test_step_argument_checks(L):
     lib = L.lib()
     assert _step(L, dims(), null=("H",)) == L.DG_EINVAL
     assert _step(L, dims(), weights_null=("E",)) == L.DG_EINVAL
-    assert _step(L, dims(), weights_null=("E_tiled",)) == L.DG_EINVAL   # bf16 needs the tiled table
     assert _step(L, dims(n_kv_heads=3)) == L.DG_EINVAL
     assert _step(L, dims(B=0)) == L.DG_EINVAL
     assert _step(L, dims(L=2000, cap=1024)) == L.DG_EINVAL
@@ -126,7 +125,7 @@ def test_step_argument_checks(L):
     assert _step(L, dims(), ws=None) == L.DG_EWORKSPACE
     assert b"workspace" in lib.dg_last_error()
     # misaligned bf16 tensor
-    w = L.Weights(FAKE, FAKE + 2, FAKE, FAKE, FAKE, FAKE)
+    w = L.Weights(FAKE, FAKE + 2, FAKE, FAKE, FAKE)
     io = L.StepIO(*[FAKE if k in ("H", "k_cache", "v_cache", "tokens_in", "tokens_out", "selfcond_out",
                                   "max_logit", "conf", "argmax") else None for k in L.STEP_IO_FIELDS])
     st = lib.dg_denoise_step(ctypes.byref(dims()), ctypes.byref(w), ctypes.byref(io), 0.9, 1, 1, 0,
@@ -152,7 +151,7 @@ def test_component_argument_checks(L):
     assert lib.dg_renoise(16, 16, 100, None, FAKE, 0.5, 1, 1, 0, FAKE, None, None) == L.DG_EINVAL
     assert lib.dg_init_canvas(16, 16, 0, 1, 0, FAKE, None) == L.DG_EINVAL
     # append beyond the cache capacity
-    w = L.Weights(FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    w = L.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
     assert lib.dg_prefill_append(ctypes.byref(dims(L=1000, cap=1024)), ctypes.byref(w), FAKE, FAKE, FAKE,
                                  FAKE, None, FAKE, 1 << 40, None) == L.DG_EINVAL
     assert b"cap" in lib.dg_last_error()
@@ -176,7 +175,7 @@ def test_tiled_embedding_sizes_and_checks(L):
 
 def test_block_loop_and_graph_argument_checks(L):
     lib = L.lib()
-    w = L.Weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    w = L.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
     io = L.BlockIO(*[FAKE if k not in ("mask", "trace_tokens", "trace_conf", "trace_selfcond") else None
                      for k in L.BLOCK_IO_FIELDS])
     taus = (ctypes.c_float * 4)(0.5, 0.6, 0.7, 0.8)
@@ -215,7 +214,7 @@ def test_masked_sampler_argument_checks(L):
     assert lib.dg_unmask(16, FAKE, FAKE, 0.5, 3, None, FAKE, None, None) == L.DG_EINVAL
     assert lib.dg_init_masked(16, 3, None, None) == L.DG_EINVAL
     assert lib.dg_init_masked(0, 3, FAKE, None) == L.DG_EINVAL
-    w = L.Weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    w = L.Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
     io = L.StepIO(*[FAKE if k in ("H", "k_cache", "v_cache", "tokens_in", "tokens_out", "selfcond_out",
                                   "max_logit", "conf", "argmax") else None for k in L.STEP_IO_FIELDS])
     for mid in (-1, 32768):   # outside [0, V)

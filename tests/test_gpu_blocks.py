@@ -42,9 +42,7 @@ class Loop:
         self.cfg, self.blocks, self.steps = c, blocks, steps
         fdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
         self.W = {k: dg.to_device(v) for k, v in p.W.items()}
-        self.W["E"] = dg.to_device(p.E)
-        if c.dtype == "bf16":
-            self.W["E_tiled"] = dg.tiled_embedding(self.W["E"])
+        self.W["E"] = dg.model_embedding(dg.to_device(p.E))
         self.Kc0 = dg.to_device(p.Kc)
         self.Vc0 = dg.to_device(p.Vc)
         self.Kc, self.Vc = self.Kc0.clone(), self.Vc0.clone()

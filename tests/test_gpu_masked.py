@@ -74,9 +74,7 @@ def test_masked_step_lockstep(cfg):
     E, H, Kc, Vc = f(p.E), f(p.H[0]), f(p.Kc), f(p.Vc)
     W = {k: f(v) for k, v in p.W.items()}
     Wd = {k: dg.to_device(v) for k, v in p.W.items()}
-    Wd["E"] = dg.to_device(p.E)
-    if cfg.dtype == "bf16":
-        Wd["E_tiled"] = dg.tiled_embedding(Wd["E"])
+    Wd["E"] = dg.model_embedding(dg.to_device(p.E))
     dt = dg.DG_BF16 if cfg.dtype == "bf16" else dg.DG_F32
     dims = dg.make_dims(cfg.B, cfg.C, cfg.L, cfg.cap, cfg.d, cfg.Hq, cfg.Hkv, cfg.dh, cfg.V, dt)
     ws = dg.workspace(dg.dg_workspace_bytes(dims))

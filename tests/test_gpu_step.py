@@ -39,8 +39,7 @@ class Dev:
         c = p.cfg
         self.cfg = c
         self.W = {k: dev(v) for k, v in p.W.items()}
-        self.W["E"] = dev(p.E)
-        self.W["E_tiled"] = dg.tiled_embedding(self.W["E"])
+        self.W["E"] = dg.model_embedding(dev(p.E))
         self.Kc = dev(p.Kc)
         self.Vc = dev(p.Vc)
         self.H = [dev(h) for h in p.H]

@@ -11,7 +11,7 @@ from ._lib import (  # noqa: F401
     lib, make_dims, workspace, ptr, dtype_code, stream_handle,
     dg_workspace_bytes, dg_attn_workspace_bytes, dg_vocab_workspace_bytes,
     dg_denoise_step, dg_attn_bidir, dg_vocab_selfcond, dg_renoise, dg_init_canvas,
-    dg_prefill_append, dg_tiled_embedding_bytes, dg_pack_embedding, tiled_embedding,
+    dg_prefill_append, dg_tiled_embedding_bytes, dg_pack_embedding, tiled_embedding, model_embedding,
     WEIGHT_FIELDS, BlockIO, BLOCK_IO_FIELDS, Graph, dg_block_loop, dg_graph_capture_block_loop,
     dg_unmask, dg_init_masked, dg_denoise_step_masked,
     dg_attn_bidir_noalloc, ATTN_NOALLOC_MAX_BYTES, dg_test_set_group_wait,

@@ -29,7 +29,7 @@ class Dims(ctypes.Structure):
                 ("B", "C", "L", "cap", "d", "n_q_heads", "n_kv_heads", "head_dim", "V", "dtype")]
 
 
-WEIGHT_FIELDS = ("Wq", "Wk", "Wv", "Wo", "E", "E_tiled")
+WEIGHT_FIELDS = ("Wq", "Wk", "Wv", "Wo", "E")
 
 
 class Weights(ctypes.Structure):
@@ -200,6 +200,13 @@ def tiled_embedding(E, stream=None):
     return out
 
 
+def model_embedding(E, stream=None):
+    """The embedding table in the form dg_weights.E takes: the tiled table
+    for a bf16 E[V][d] (a new tensor; the row-major one can then be freed),
+    E itself for float32."""
+    return tiled_embedding(E, stream) if E.dtype == torch.bfloat16 else E
+
+
 _FLOAT_IO = ("H", "k_cache", "v_cache", "selfcond_in", "selfcond_out", "x_out", "q_out",
              "k_new_out", "v_new_out", "attn_out", "z_out")
 
@@ -212,9 +219,9 @@ def _check_float_dtype(dims, tensors):
 
 
 def dg_denoise_step(dims, weights, io, tau, seed, t, block, ws, stream=None):
-    """weights: dict Wq, Wk, Wv, Wo, E (and E_tiled for bf16, see
-    tiled_embedding); io: dict with the dg_step_io fields (missing keys ->
-    NULL).  ws: uint8 workspace tensor."""
+    """weights: dict Wq, Wk, Wv, Wo, E (E as model_embedding returns it: the
+    tiled table for bf16); io: dict with the dg_step_io fields (missing keys
+    -> NULL).  ws: uint8 workspace tensor."""
     _check_float_dtype(dims, [(k, weights.get(k)) for k in WEIGHT_FIELDS] +
                        [(k, io.get(k)) for k in _FLOAT_IO])
     for k in ("tokens_in", "tokens_out", "argmax"):

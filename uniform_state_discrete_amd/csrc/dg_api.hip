@@ -124,8 +124,8 @@ int check_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io, c
   int st = check_dims(dims, true);
   if (st != DG_OK) return st;
   if (!w || !io) return fail(DG_EINVAL, "weights and io must be non-NULL");
-  if (!w->Wq || !w->Wk || !w->Wv || !w->Wo || !w->E || (dims->dtype == DG_BF16 && !w->E_tiled))
-    return fail(DG_EINVAL, "every weight pointer (and E_tiled for bf16) must be non-NULL");
+  if (!w->Wq || !w->Wk || !w->Wv || !w->Wo || !w->E)
+    return fail(DG_EINVAL, "every weight pointer must be non-NULL");
   if (!io->H || !io->tokens_in || !io->tokens_out || !io->selfcond_out || !io->max_logit ||
       !io->conf || !io->argmax || (dims->L > 0 && (!io->k_cache || !io->v_cache)))
     return fail(DG_EINVAL, "H, tokens_in/out, selfcond_out, max_logit, conf, argmax (and the caches when L > 0) must be non-NULL");
@@ -135,8 +135,8 @@ int check_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io, c
     return fail(DG_EUNSUPPORTED, "bf16 step needs d %% 128 == 0 and n_q_heads*head_dim %% 64 == 0");
   const void* ptrs[] = {w->Wq, w->Wk, w->Wv, w->Wo, w->E, io->H, io->k_cache, io->v_cache,
                         io->selfcond_in, io->selfcond_out, io->x_out, io->q_out, io->k_new_out,
-                        io->v_new_out, io->attn_out, io->z_out, w->E_tiled};
-  if ((st = check_bf16_align(dims, ptrs, 17)) != DG_OK) return st;
+                        io->v_new_out, io->attn_out, io->z_out};
+  if ((st = check_bf16_align(dims, ptrs, 16)) != DG_OK) return st;
   const StepLayout L = step_layout(dims);
   if (!ws || ws_bytes < L.total)
     return fail(DG_EWORKSPACE, "step workspace needs %zu bytes (got %zu)", L.total, ws ? ws_bytes : 0);
@@ -177,7 +177,7 @@ int enqueue_step(const dg_dims* dims, const dg_weights* w, const dg_step_io* io,
     return hip_fail(e, "output projection");
   // the uniform-state renoise rides on the vocabulary head's split combine
   const dg::RenoiseArgs rn{io->tokens_out, io->mask, tau, seed, t, block, dims->C, dims->V};
-  if ((e = dg::launch_vocab(vp, Z, dt == DG_BF16 ? w->E_tiled : w->E, io->max_logit, io->argmax, io->conf, io->lse, io->selfcond_out,
+  if ((e = dg::launch_vocab(vp, Z, w->E, io->max_logit, io->argmax, io->conf, io->lse, io->selfcond_out,
                             scratch, s, (hipEvent_t)io->ev_vocab_begin, (hipEvent_t)io->ev_vocab_end,
                             mask_id >= 0 ? nullptr : &rn, xbytes > 0)) != hipSuccess)
     return hip_fail(e, "vocab/self-conditioning/renoise");

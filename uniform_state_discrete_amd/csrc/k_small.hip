@@ -10,9 +10,13 @@ namespace dg {
 // self-conditioning vector handed over from the previous step
 // (DiffusionGemma explainer, "Autocondizionamento").  One rounding to the
 // storage type (bf16: fp32 sum; fp32: fp64 sum).  One workgroup per row.
+// bf16 reads the token's row from the tiled table (the only copy of E the
+// bf16 path keeps): columns 32c + 8g .. +7 of id 16 vb + i are the 16 bytes at
+// lane position 16 g + i of 1 KiB block (vb, c), the two 8-byte halves
+// swapped for odd g.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) k_assemble_bf16(int d, int V, const u16* __restrict__ H,
-                                                       const u16* __restrict__ E,
+                                                       const u16* __restrict__ Et,
                                                        const int32_t* __restrict__ x,
                                                        const u16* __restrict__ S,
                                                        u16* __restrict__ X) {
@@ -20,10 +24,12 @@ __global__ void __launch_bounds__(256) k_assemble_bf16(int d, int V, const u16* 
   int tok = x[r];
   if (tok < 0 || tok >= V) tok = 0;
   const size_t ro = (size_t)r * d;
-  const size_t eo = (size_t)tok * d;
+  const size_t vb = (size_t)(tok >> 4) * (d >> 5), id = (size_t)(tok & 15);
   for (int e = threadIdx.x * 8; e < d; e += 256 * 8) {
+    const int c = e >> 5, g = (e >> 3) & 3;
     u32x4 h = ldg128(H + ro + e);
-    u32x4 em = ldg128(E + eo + e);
+    u32x4 em = ldg128(Et + (vb + c) * 512 + 8 * (16 * g + id));
+    if (g & 1) em = u32x4{em[2], em[3], em[0], em[1]};
     u32x4 s = {0u, 0u, 0u, 0u};
     if (S) s = ldg128(S + ro + e);
     u32x4 o;
