@@ -191,3 +191,36 @@ def test_block_append_and_next_block(cfg):
     ref = step.denoise_step(h["H"][1], h["E"], h["W"], f64(g.Kc), f64(g.Vc), L1, x.cpu().numpy(), None,
                             c.tau[1], c.seed, 1, 1, c.dtype)
     compare_full(c, o, ref, h["E"], c.tau[1], "block 1 step 0")
+
+
+def test_prefill_append_prompt4096_every_element():
+    """The causal prefill of a 4096-token prompt into an empty cache, the shape
+    bench.py times (the full-vocabulary workload's model: d = 2048, 16/8 heads
+    of 128): every appended K/V cache row and every element of the causal
+    attention output against the oracle's prefill-append."""
+    import uniform_state_discrete_amd as dg
+    c = config_by_name("canvas256_L8192_d2048_V262144")
+    n = 4096
+    say(f"prefill-append of a {n}-token prompt, every element")
+    p = gen_problem(c)
+    W = {k: dev(v) for k, v in p.W.items()}
+    W["E"] = dg.model_embedding(dev(p.E))
+    rng = np.random.default_rng(4096)
+    Hs = np.tile(p.H[0].reshape(c.C, c.d), (n // c.C, 1)).reshape(1, n, c.d)   # stored bf16 bits
+    toks = rng.integers(0, c.V, (1, n)).astype(np.int32)
+    dims = dg.make_dims(1, n, 0, n, c.d, c.Hq, c.Hkv, c.dh, c.V, dg.DG_BF16)
+    ws = dg.workspace(dg.dg_workspace_bytes(dims))
+    Kc = torch.zeros((1, c.Hkv, n, c.dh), dtype=torch.bfloat16, device="cuda")
+    Vc = torch.zeros_like(Kc)
+    attn = torch.empty((1, n, c.Hq, c.dh), dtype=torch.bfloat16, device="cuda")
+    dg.dg_prefill_append(dims, W, dev(Hs), dev(toks), Kc, Vc, attn, ws)
+    torch.cuda.synchronize()
+    f = lambda a: as_f64(a, c.dtype)
+    E = f(p.E)
+    Wf = {k: f(v) for k, v in p.W.items()}
+    del p
+    z = np.zeros((1, c.Hkv, n, c.dh))
+    K2, V2, rO, _ = step.prefill_append(f(Hs), E, Wf, z, z, 0, toks, c.dtype)
+    close_rel("appended K, 4096 rows", f64(Kc), K2, 2.0 ** -6)
+    close_rel("appended V, 4096 rows", f64(Vc), V2, 2.0 ** -6)
+    close("causal O", f64(attn), rO, ATOL[c.dtype], RELF[c.dtype], bf16_ulp=True)

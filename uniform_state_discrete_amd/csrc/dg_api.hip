@@ -221,12 +221,10 @@ int enqueue_append(const dg_dims* dims, const dg_weights* w, const void* H, cons
   hipError_t e;
   if ((e = dg::launch_assemble(dt, R, d, dims->V, H, w->E, tokens_final, nullptr, X, s)) != hipSuccess)
     return hip_fail(e, "assemble");
-  if ((e = dg::launch_gemm_qkv(dt, R, d, X, w->Wq, Hq * dh, Q, w->Wk, w->Wv, Hkv * dh, Kn, Vn, s)) != hipSuccess)
-    return hip_fail(e, "Q/K/V projections");
-  if ((e = dg::launch_cache_append(dt, dims->B, dims->C, dims->L, dims->cap, Hkv, dh, Kn, k_cache, s)) != hipSuccess)
-    return hip_fail(e, "K cache append");
-  if ((e = dg::launch_cache_append(dt, dims->B, dims->C, dims->L, dims->cap, Hkv, dh, Vn, v_cache, s)) != hipSuccess)
-    return hip_fail(e, "V cache append");
+  // the projection's epilogue also writes K_new / V_new into cache rows [L, L + C)
+  if ((e = dg::launch_gemm_qkv(dt, R, d, X, w->Wq, Hq * dh, Q, w->Wk, w->Wv, Hkv * dh, Kn, Vn, s, k_cache, v_cache,
+                               dg::CacheGeom{dims->C, dims->L, dims->cap, dh})) != hipSuccess)
+    return hip_fail(e, "Q/K/V projections and cache write");
   dg::AttnPlan ap = dg::attn_plan(dims->B, dims->C, dims->L, dims->cap, Hq, Hkv, dh, dt, 1);
   if ((e = dg::launch_attn(ap, Q, k_cache, v_cache, Kn, Vn, O, nullptr, at(ws, L.scratch), s)) != hipSuccess)
     return hip_fail(e, "causal attention");

@@ -148,6 +148,14 @@ struct GemmSeg {
   const u16* Res;
   u16* C;
   int N, tiles;
+  // optional second destination of the output: a KV cache [B][N/dh][cap][dh]
+  // whose rows [L, L + Cn) of every (canvas, head) take output rows
+  // b Cn + i (the cache write of a prefill-append); NULL: none
+  u16* cache;
+};
+// Geometry of GemmSeg::cache (canvas length Cn, first row L, capacity, head dim).
+struct CacheGeom {
+  int Cn, L, cap, dh;
 };
 // bf16: zero_bytes (a multiple of 16) at zero are also cleared by the same
 // launch, for a kernel later on the stream.
@@ -155,9 +163,12 @@ hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const v
                           const void* Res, void* C, hipStream_t s, void* zero = nullptr,
                           size_t zero_bytes = 0);
 // Q, K and V projections of the same activations in one launch (bf16), or
-// three launches (fp32).
+// three launches (fp32).  bf16 with k_cache / v_cache set: the K and V
+// outputs are also written to those caches at rows [g.L, g.L + g.Cn) by the
+// same launch (fp32: by separate cache-append launches).
 hipError_t launch_gemm_qkv(int dtype, int M, int K, const void* A, const void* Wq, int Nq, void* Q,
-                           const void* Wk, const void* Wv, int Nkv, void* Kn, void* Vn, hipStream_t s);
+                           const void* Wk, const void* Wv, int Nkv, void* Kn, void* Vn, hipStream_t s,
+                           void* k_cache = nullptr, void* v_cache = nullptr, CacheGeom g = CacheGeom{1, 0, 1, 1});
 
 hipError_t launch_assemble(int dtype, int R, int d, int V, const void* H, const void* E,
                            const int32_t* x, const void* S, void* X, hipStream_t s);

@@ -19,9 +19,19 @@ namespace dg {
 // projections read the same activations).
 constexpr int GKS = 64, GLD = GKS + 8;  // K slice; LDS row of 144 bytes: conflict-free
 
+// The cache copy of output element(s) of row am, columns n .. n+cnt-1 (within
+// one head: dh is a multiple of 4 and n of 4): cache[b][g][L + i][e] with
+// am = b Cn + i, n = g dh + e (the prefill-append's cache write, fused into
+// the projection's epilogue).
+__device__ __forceinline__ u16* cache_row(u16* cache, const CacheGeom& cg, int N, int am, int n) {
+  const int b = am / cg.Cn, i = am - b * cg.Cn;
+  const int g = n / cg.dh, e = n - g * cg.dh;
+  return cache + (((size_t)b * (N / cg.dh) + g) * cg.cap + cg.L + i) * cg.dh + e;
+}
+
 __global__ void __launch_bounds__(256) k_gemm_nt_bf16(int M, int K, const u16* __restrict__ A, GemmSeg s0,
                                                       GemmSeg s1, GemmSeg s2, u32x4* __restrict__ zp,
-                                                      size_t zn16) {
+                                                      size_t zn16, CacheGeom cg) {
   if (zp) {
     // a region a later kernel needs zeroed, spread over every thread of the grid
     const size_t nth = (size_t)gridDim.x * gridDim.y * blockDim.x;
@@ -124,11 +134,13 @@ __global__ void __launch_bounds__(256) k_gemm_nt_bf16(int M, int K, const u16* _
       }
       u32x2 out = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       *(u32x2*)(C + o) = out;
+      if (sg.cache) *(u32x2*)cache_row(sg.cache, cg, N, am, n) = out;
     } else {
       for (int i = 0; i < 4 && n + i < N; ++i) {
         float x = v[i];
         if (Res) x += bf16_to_f32(Res[o + i]);
         C[o + i] = (u16)f32_to_bf16(x);
+        if (sg.cache) *cache_row(sg.cache, cg, N, am, n + i) = (u16)f32_to_bf16(x);
       }
     }
   }
@@ -142,7 +154,7 @@ __global__ void __launch_bounds__(256) k_gemm_nt_bf16(int M, int K, const u16* _
 // two slices in flight through registers.
 __global__ void __launch_bounds__(256) k_gemm_nt_bf16_t128(int M, int K, const u16* __restrict__ A, GemmSeg s0,
                                                            GemmSeg s1, GemmSeg s2, u32x4* __restrict__ zp,
-                                                           size_t zn16) {
+                                                           size_t zn16, CacheGeom cg) {
   if (zp) {
     const size_t nth = (size_t)gridDim.x * gridDim.y * blockDim.x;
     for (size_t i = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; i < zn16; i += nth)
@@ -245,11 +257,13 @@ __global__ void __launch_bounds__(256) k_gemm_nt_bf16_t128(int M, int K, const u
           }
           u32x2 out = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *(u32x2*)(C + o) = out;
+          if (sg.cache) *(u32x2*)cache_row(sg.cache, cg, N, am, n) = out;
         } else {
           for (int i = 0; i < 4 && n + i < N; ++i) {
             float x = v[i];
             if (Res) x += bf16_to_f32(Res[o + i]);
             C[o + i] = (u16)f32_to_bf16(x);
+            if (sg.cache) *cache_row(sg.cache, cg, N, am, n + i) = (u16)f32_to_bf16(x);
           }
         }
       }
@@ -285,8 +299,8 @@ __global__ void __launch_bounds__(256) k_gemm_nt_f32(int M, int N, int K, const 
 // Row count from which the 128 x 128 tile kernel runs.
 constexpr int kGemmBigM = 1024;
 
-static GemmSeg gemm_seg(const void* B, const void* Res, void* C, int N, int tn) {
-  return GemmSeg{(const u16*)B, (const u16*)Res, (u16*)C, N, (N + tn - 1) / tn};
+static GemmSeg gemm_seg(const void* B, const void* Res, void* C, int N, int tn, void* cache = nullptr) {
+  return GemmSeg{(const u16*)B, (const u16*)Res, (u16*)C, N, (N + tn - 1) / tn, (u16*)cache};
 }
 
 hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const void* B,
@@ -294,14 +308,15 @@ hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const v
   if (M <= 0 || N <= 0) return hipSuccess;
   if (dtype == 1) {
     const int tn = M >= kGemmBigM ? 128 : 64;
-    const GemmSeg s0 = gemm_seg(B, Res, C, N, tn), none = GemmSeg{nullptr, nullptr, nullptr, 0, 0};
+    const GemmSeg s0 = gemm_seg(B, Res, C, N, tn), none = GemmSeg{nullptr, nullptr, nullptr, 0, 0, nullptr};
+    const CacheGeom cg{1, 0, 1, 1};
     dim3 grid((unsigned)s0.tiles, (M + tn - 1) / tn);
     if (tn == 128)
       hipLaunchKernelGGL(k_gemm_nt_bf16_t128, grid, dim3(256), 0, s, M, K, (const u16*)A, s0, none, none,
-                         (u32x4*)zero, zero_bytes / 16);
+                         (u32x4*)zero, zero_bytes / 16, cg);
     else
       hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, s0, none, none, (u32x4*)zero,
-                         zero_bytes / 16);
+                         zero_bytes / 16, cg);
   } else {
     dim3 grid((N + 15) / 16, (M + 15) / 16);
     hipLaunchKernelGGL(k_gemm_nt_f32, grid, dim3(256), 0, s, M, N, K, (const float*)A,
@@ -311,23 +326,29 @@ hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const v
 }
 
 hipError_t launch_gemm_qkv(int dtype, int M, int K, const void* A, const void* Wq, int Nq, void* Q,
-                           const void* Wk, const void* Wv, int Nkv, void* Kn, void* Vn, hipStream_t s) {
+                           const void* Wk, const void* Wv, int Nkv, void* Kn, void* Vn, hipStream_t s,
+                           void* k_cache, void* v_cache, CacheGeom g) {
   if (M <= 0) return hipSuccess;
   if (dtype != 1) {
     hipError_t e = launch_gemm_nt(dtype, M, Nq, K, A, Wq, nullptr, Q, s);
     if (e == hipSuccess) e = launch_gemm_nt(dtype, M, Nkv, K, A, Wk, nullptr, Kn, s);
     if (e == hipSuccess) e = launch_gemm_nt(dtype, M, Nkv, K, A, Wv, nullptr, Vn, s);
+    if (e == hipSuccess && k_cache)
+      e = launch_cache_append(dtype, M / g.Cn, g.Cn, g.L, g.cap, Nkv / g.dh, g.dh, Kn, k_cache, s);
+    if (e == hipSuccess && v_cache)
+      e = launch_cache_append(dtype, M / g.Cn, g.Cn, g.L, g.cap, Nkv / g.dh, g.dh, Vn, v_cache, s);
     return e;
   }
   const int tn = M >= kGemmBigM ? 128 : 64;
-  const GemmSeg sq = gemm_seg(Wq, nullptr, Q, Nq, tn), sk = gemm_seg(Wk, nullptr, Kn, Nkv, tn),
-                sv = gemm_seg(Wv, nullptr, Vn, Nkv, tn);
+  const GemmSeg sq = gemm_seg(Wq, nullptr, Q, Nq, tn), sk = gemm_seg(Wk, nullptr, Kn, Nkv, tn, k_cache),
+                sv = gemm_seg(Wv, nullptr, Vn, Nkv, tn, v_cache);
   dim3 grid((unsigned)(sq.tiles + sk.tiles + sv.tiles), (M + tn - 1) / tn);
   if (tn == 128)
     hipLaunchKernelGGL(k_gemm_nt_bf16_t128, grid, dim3(256), 0, s, M, K, (const u16*)A, sq, sk, sv, nullptr,
-                       (size_t)0);
+                       (size_t)0, g);
   else
-    hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, sq, sk, sv, nullptr, (size_t)0);
+    hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, sq, sk, sv, nullptr, (size_t)0,
+                       g);
   return hipGetLastError();
 }
 
