@@ -674,12 +674,17 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
       for (int c = 0; c < NCH; ++c) zf[h][c] = swap_halves(ldg128(zp + 32 * c), g & 1);
     }
-    u32x4 ring[NCH];
+    // E chunks stream through a register ring of PF slots: chunk c of a tile
+    // sits in slot c % PF and is loaded PF chunks ahead (a whole tile ahead
+    // for pairs; half a tile for quads, whose three exchange records leave
+    // no room for eight slots)
+    constexpr int PF = Q == 2 ? NCH : NCH / 2;
+    u32x4 ring[PF];
     auto issue = [&](int c, int step) {
-      ring[c] = buffer_ld128(erc, lane_off + (uint32_t)phys(step) * blk_row + 1024u * c);
+      ring[c % PF] = buffer_ld128(erc, lane_off + (uint32_t)phys(step) * blk_row + 1024u * c);
     };
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) issue(c, 0);
+    for (int c = 0; c < PF; ++c) issue(c, 0);
     tr_load((const DG_LDS u16*)&Et[1][w][0][0], 0, 0);  // tile -3: zeros
     tr_load((const DG_LDS u16*)&Et[1][w][0][0], 1, 1);
 
@@ -848,7 +853,7 @@ __global__ void __launch_bounds__(256, 1)
       };
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const u32x4 e = ring[c];
+        const u32x4 e = ring[c % PF];
         if (c == 0) {
           // tile t-1's partial logits of this wave (finished last iteration)
 #pragma unroll
@@ -901,8 +906,12 @@ __global__ void __launch_bounds__(256, 1)
           tr_load(tpe, c + 2, c & 1);
         else
           tr_load(tnx, c + 2 - NCH, c & 1);
-        // chunk c of tile t+1 into the slot this chunk's products just read
-        issue(c, t + 1);
+        // the chunk PF ahead (of this tile or of tile t+1) into the slot this
+        // chunk's products just read
+        if (c + PF < NCH)
+          issue(c + PF, t);
+        else
+          issue(c + PF - NCH, t + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
