@@ -309,11 +309,12 @@ def run_workload(cfg, steps, warmup, replays, stream, keep_problem=False, settle
       - settle: the chained step runs untimed for settle_s seconds, then the
         canvas is drawn again, so the timed steps start from the same state;
       - `warmup` untimed steps;
-      - eager: `steps` steps between HIP events on the launch stream, with
-        the per-kernel event hooks of the attention and flash-vocab kernels;
-      - graph: the same `steps` steps captured once into a HIP graph and
-        replayed `replays` times, each replay timed with HIP events; median,
-        p10 and p90 of the time per step.
+      - graph: the `steps` steps captured once into a HIP graph and replayed
+        `replays` times, each replay timed with HIP events; median, p10 and
+        p90 of the time per step (the headline);
+      - eager, right after: the same `steps` steps between HIP events on the
+        launch stream, with the per-kernel event hooks of the attention and
+        flash-vocab kernels (the roofline's kernel time).
     Inputs are generated and uploaded before any timed region."""
     import numpy as np
     import torch
@@ -367,6 +368,32 @@ def run_workload(cfg, steps, warmup, replays, stream, keep_problem=False, settle
         run(s, stream)
     torch.cuda.synchronize()
     kept = [1.0 - float(stats["mask"].float().mean())]
+
+    # the chained steps as one HIP graph, replayed: the headline time
+    # (replays = 0: no graph; the eager time stands in, for profiler runs)
+    per_step = []
+    if replays > 0:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(g, stream=cap, capture_error_mode="relaxed"):
+            for k in range(steps):
+                run(k, cap)
+        torch.cuda.synchronize()
+        g.replay()                                   # warm-up replay
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream()
+        for _ in range(replays):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            g.replay()
+            e1.record(cur)
+            torch.cuda.synchronize()
+            per_step.append(e0.elapsed_time(e1) / steps)
+        del g
+
+    # right after, the same steps eager with HIP events around the attention
+    # and flash-vocab kernels on the launch stream: the per-kernel times
     t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
     t0e.record(stream)
@@ -380,27 +407,8 @@ def run_workload(cfg, steps, warmup, replays, stream, keep_problem=False, settle
     vocab_ms = [ev["vb"][k].elapsed_time(ev["ve"][k]) for k in range(steps)]
     attn_ms = [ev["ab"][k].elapsed_time(ev["ae"][k]) for k in range(steps)]
 
-    # the same steps as one HIP graph, replayed
-    g = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    with torch.cuda.graph(g, stream=cap, capture_error_mode="relaxed"):
-        for k in range(steps):
-            run(k, cap)
-    torch.cuda.synchronize()
-    g.replay()                                   # warm-up replay
-    torch.cuda.synchronize()
-    per_step = []
-    cur = torch.cuda.current_stream()
-    for _ in range(replays):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(cur)
-        g.replay()
-        e1.record(cur)
-        torch.cuda.synchronize()
-        per_step.append(e0.elapsed_time(e1) / steps)
-    del g
-
+    if not per_step:
+        per_step = [ms_eager]
     alg = algorithmic(cfg)
     v_avg = float(np.mean(vocab_ms))
     a_avg = float(np.mean(attn_ms))
@@ -442,7 +450,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--replays", type=int, default=10, help="timed graph replays of the steps")
+    ap.add_argument("--replays", type=int, default=10,
+                    help="timed graph replays of the steps (0: no graph phase, eager time only)")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed chained steps before each workload's warm-up")
+    ap.add_argument("--block-loop-only", action="store_true",
+                    help="only time the block-diffusion graph replay (one JSON object)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn-hbm", action="store_true", help="skip the HBM-bound attention shape")
@@ -471,10 +484,15 @@ def main():
 
     from synth import config_by_name
 
+    if args.block_loop_only:
+        torch.cuda.set_device(0)
+        print(json.dumps({"block_loop_graph": block_loop_graph(torch.cuda.Stream())}), flush=True)
+        return
     cfg = config_by_name(args.workload)
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
-    r, keep = run_workload(cfg, args.steps, args.warmup, args.replays, stream, keep_problem=True)
+    r, keep = run_workload(cfg, args.steps, args.warmup, args.replays, stream, keep_problem=True,
+                           settle_s=args.settle)
     p, W, H = keep
     out = {
         "metric": "canvas denoise steps/s (256 tok, V=262144) + % MFMA peak, % HBM peak",
@@ -493,7 +511,8 @@ def main():
                    "d_model": cfg.d, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.dh,
                    "vocab": cfg.V, "tau": cfg.tau[0], "parallelism": "1 GPU"},
         "timing": "median of the graph replays (each replays the chained steps); p10/p90 beside it; "
-                  f"before the warm-up steps the step runs untimed for {SETTLE_S} s (settle_steps)",
+                  f"before the warm-up steps the step runs untimed for {args.settle} s (settle_steps); "
+                  "the roofline's kernel time is the mean over eager steps run right after the replays",
     }
     for k in ("ms_per_step_p10", "ms_per_step_p90", "graph_replays", "settle_steps", "ms_per_step_eager", "canvas_tokens_per_s",
               "step_mfma_frac", "step_hbm_frac", "flash_vocab_ms", "flash_vocab_ms_p10", "flash_vocab_ms_p90",
@@ -503,7 +522,7 @@ def main():
     if not args.no_other_workloads and args.workload == DEFAULT_WORKLOAD:
         others = []
         for name, steps in (("canvas256_L1024_d2048_V32768", 16), ("canvas256_L32768_d4096_V262144", 8)):
-            o, _ = run_workload(config_by_name(name), steps, 2, 5, stream)
+            o, _ = run_workload(config_by_name(name), steps, 2, 5, stream, settle_s=args.settle)
             others.append(rounded({k: o[k] for k in ("workload", "steps", "steps_per_s", "ms_per_step",
                                                      "ms_per_step_p10", "ms_per_step_p90", "ms_per_step_eager",
                                                      "canvas_tokens_per_s", "step_mfma_frac", "flash_vocab_ms",
