@@ -174,6 +174,55 @@ def test_vocab_group_solo_equals_paired(R, d, V):
         argmax_match("argmax", got[1], ra, gap, rm)
 
 
+def test_vocab_group_beside_a_concurrent_kernel():
+    """A long matrix product on another stream holds CUs while the vocabulary
+    head starts, so the members of a CU group are dispatched as CUs free up
+    and may wait for each other; whatever the handshake then decides (on this
+    box the members arrived within its bound: paired), the outputs are the
+    bits of an undisturbed run.  The number of members that ran solo is read
+    from the exchange header (word 16) and reported."""
+    import uniform_state_discrete_amd as dg
+    R, d, V = 256, 2048, 262144
+    say("vocab beside a concurrent kernel")
+    E, Z = _vocab_inputs(R, d, V, "bf16", seed=77)
+    Ed, Zd = dev(E), dev(Z)
+    Et = dg.tiled_embedding(Ed)
+    del Ed
+    nbytes = dg.dg_vocab_workspace_bytes(R, d, V, Zd.dtype)
+    ws = dg.workspace(nbytes)
+
+    def run(stream):
+        out = [torch.empty(R, device="cuda") for _ in range(3)]
+        a = torch.empty(R, dtype=torch.int32, device="cuda")
+        S = torch.empty((R, d), dtype=torch.bfloat16, device="cuda")
+        dg.dg_vocab_selfcond(R, d, V, Zd, Et, out[0], a, out[1], out[2], S, ws, stream)
+        return out + [a, S]
+
+    ref = run(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    # exchange header: after the partials of S (2 nsplit R d fp32) and the
+    # per-row split statistics (nsplit R x 16 bytes), 256-byte aligned; 32
+    # splits of 8192 ids at these sizes
+    nsplit = 32
+    hdr = (2 * nsplit * R * d * 4 + nsplit * R * 16 + 255) // 256 * 256
+    side = torch.cuda.Stream()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    A = torch.randn(8192, 8192, generator=g, device="cuda").to(torch.bfloat16)
+    solo = []
+    for rep in range(4):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                C = A @ A                              # holds CUs for milliseconds
+        got = run(torch.cuda.current_stream())      # not ordered after the side stream
+        torch.cuda.synchronize()
+        solo.append(int(ws[hdr + 64:hdr + 68].view(torch.int32).item()))
+        for name, u, v in zip(("max_logit", "conf", "lse", "argmax", "S"), got, ref):
+            assert torch.equal(u, v), f"run {rep}: {name} differs from the undisturbed run"
+        del C
+    say(f"members that ran solo per run: {solo} (of 256)")
+
+
 @pytest.mark.parametrize("d,dtype", [(256, "bf16"), (2048, "bf16"), (4096, "bf16"), (64, "f32")])
 def test_vocab_one_hot_is_exact_embedding_lookup(d, dtype):
     V, R = 3000, 40
