@@ -367,9 +367,14 @@ __device__ __forceinline__ f32x4 pair_tagged(f32x4 v, uint32_t gen) {
   for (int i = 0; i < 4; ++i) o[i] = __uint_as_float((__float_as_uint(v[i]) & ~1u) | gen);
   return o;
 }
+// all four tag bits equal gen: with m = gen - 1 (0, or all ones for gen 0),
+// bit 0 of the AND of the words xor m is set
 __device__ __forceinline__ bool pair_gen_ok(u32x4 w, uint32_t gen) {
-  return ((w[0] & w[1] & w[2] & w[3] & 1u) == gen) & (((w[0] | w[1] | w[2] | w[3]) & 1u) == gen);
+  const uint32_t m = gen - 1u;
+  return (((w[0] ^ m) & (w[1] ^ m) & (w[2] ^ m) & (w[3] ^ m)) & 1u) != 0;
 }
+// true when ok holds in every lane of the wave (all lanes are active here)
+__device__ __forceinline__ bool wave_all(bool ok) { return __builtin_amdgcn_ballot_w64(!ok) == 0; }
 __device__ __forceinline__ u32x4 pair_load(const char* base, uint32_t off) {
   uint64_t* p = (uint64_t*)(const_cast<char*>(base) + off);
   const uint64_t a = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -434,7 +439,7 @@ __global__ void __launch_bounds__(256, 1)
   __shared__ __attribute__((aligned(16))) f32x4 ownb[256];          // this member's partial, owner lane
   __shared__ int role[3];
 
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, r = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, g = l >> 4, r = l & 15;
   const int h2 = l >> 5, m32 = l & 31;
   if (threadIdx.x == 0) {
     const uint32_t xcc = __builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xFu;  // HW_REG_XCC_ID
@@ -642,7 +647,7 @@ __global__ void __launch_bounds__(256, 1)
         *(DG_LDS u32x2*)((DG_LDS char*)&Pbuf[q >> 1][orow] + 8 * (q & 1)) = u32x2{lo, hi};
       }
       Sbuf[threadIdx.x >> 2] = sc;
-      flags[__builtin_amdgcn_readfirstlane(w)] = __any(sc != 1.f) ? 1 : 0;
+      flags[w] = __any(sc != 1.f) ? 1 : 0;
       __syncthreads();
       pf[0] = Pbuf[h2][m32];
       pf[1] = Pbuf[h2][32 + m32];
@@ -756,16 +761,14 @@ __global__ void __launch_bounds__(256, 1)
           const uint32_t want = pair_gen(t - 2);
 #pragma unroll
           for (int k = 0; k < Q - 1; ++k) {
-            bool ok = pair_gen_ok(xp[k], want);
-            if (!__all(ok) && !broken) {
+            if (!wave_all(pair_gen_ok(xp[k], want)) && !broken) {
               if (l == 0) __hip_atomic_fetch_add(&xhdr[9], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               uint32_t xl = xlane;
               asm volatile("" : "+v"(xl));
               const uint32_t so = xo_in(k) + ((t - 2) & 3) * 4096u + xl;
               for (uint32_t n = 0;; ++n) {
                 xp[k] = pair_load(xbase, so);
-                ok = pair_gen_ok(xp[k], want);
-                if (__all(ok)) break;
+                if (wave_all(pair_gen_ok(xp[k], want))) break;
                 if (n >= kPairSpin) {
                   broken = true;
                   if (l == 0) {
@@ -784,33 +787,41 @@ __global__ void __launch_bounds__(256, 1)
           }
         }
         if (c == 4 && j == 1) {
-          // every member adds the Q partials in member order
+          // every member adds the Q partials in member order (for two members
+          // own + other is that sum: the addition commutes exactly)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float a = mb == 0 ? own_old[i] : __uint_as_float(xp[0][i]);
+            if constexpr (Q == 2) {
+              x[i] = own_old[i] + __uint_as_float(xp[0][i]);
+            } else {
+              float a = mb == 0 ? own_old[i] : __uint_as_float(xp[0][i]);
 #pragma unroll
-            for (int m = 1; m < Q; ++m)
-              a += m == mb ? own_old[i] : __uint_as_float(xp[m - (m > mb ? 1 : 0)][i]);
-            x[i] = a;
+              for (int m = 1; m < Q; ++m)
+                a += m == mb ? own_old[i] : __uint_as_float(xp[m - (m > mb ? 1 : 0)][i]);
+              x[i] = a;
+            }
           }
         }
         if (c == 4 && j == 2 && !(sm_ok && v2 + 16 <= ve)) {
           // a ragged or absent tile (uniform): ids past the split are -inf
+          const int lim = sm_ok ? ve - v2 : 0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[i] = sm_ok && v2 + 4 * q + i < ve ? x[i] : -INFINITY;
+          for (int i = 0; i < 4; ++i) x[i] = 4 * q + i < lim ? x[i] : -INFINITY;
         }
         if (c == 4 && j == 3) tm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        if (c == 4 && j == 4) tm = fmaxf(tm, dpp_f<0xB1>(tm));
-        if (c == 4 && j == 5) tm = fmaxf(tm, dpp_f<0x4E>(tm));  // the row's tile max, in all 4 lanes
+        if (c == 4 && j == 4) tm = dpp_max_x1(tm);
+        if (c == 4 && j == 5) tm = dpp_max_x2(tm);  // the row's tile max, in all 4 lanes
         if (c == 5 && j == 0 && __any(tm >= m_true)) {
           // the running max may move (uniform branch, rare after a split's
           // first tiles): lowest id attaining the tile max; tiles come out of
-          // id order, so a tie goes to the lower id
+          // id order, so a tie goes to the lower id.  The offset within the
+          // tile is reduced, then the tile's first id added.
           int cand = 0x7FFFFFFF;
 #pragma unroll
-          for (int i = 3; i >= 0; --i) cand = x[i] == tm ? v2 + 4 * q + i : cand;
+          for (int i = 3; i >= 0; --i) cand = x[i] == tm ? 4 * q + i : cand;
           cand = min(cand, dpp_i<0xB1>(cand));
           cand = min(cand, dpp_i<0x4E>(cand));
+          cand += v2;
           const bool better = (tm > m_true) | ((tm == m_true) & (tm != -INFINITY) & (cand < amax));
           amax = better ? cand : amax;
           m_true = fmaxf(m_true, tm);
@@ -848,7 +859,7 @@ __global__ void __launch_bounds__(256, 1)
           // every lane of a row writes the same factor, every lane of the wave
           // the same flag (no branch; orow = threadIdx.x / 4)
           Sbuf[threadIdx.x >> 2] = s;
-          flags[__builtin_amdgcn_readfirstlane(w)] = __any(s != 1.f) ? 1 : 0;
+          flags[w] = __any(s != 1.f) ? 1 : 0;
         }
       };
 #pragma unroll

@@ -111,6 +111,20 @@ template <int CTRL>
 __device__ __forceinline__ int dpp_i(int x) {
   return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
 }
+// max(x, x of the lane 1 apart / 2 apart within each group of 4 lanes), one
+// DPP instruction each.  The compiler's own form adds NaN-quieting moves around
+// every max; these operands are never NaN (finite logits or -inf).  The leading
+// wait states cover a VALU write of x just before the DPP read.
+__device__ __forceinline__ float dpp_max_x1(float x) {
+  float r;
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));
+  return r;
+}
+__device__ __forceinline__ float dpp_max_x2(float x) {
+  float r;
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));
+  return r;
+}
 template <int CTRL>
 __device__ __forceinline__ void argmax_step(float& m, int& a) {
   const float om = dpp_f<CTRL>(m);
