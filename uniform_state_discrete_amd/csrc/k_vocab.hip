@@ -369,9 +369,14 @@ __device__ __forceinline__ f32x4 pair_tagged(f32x4 v, uint32_t gen) {
 }
 // all four tag bits equal gen: with m = gen - 1 (0, or all ones for gen 0),
 // bit 0 of the AND of the words xor m is set
+// (v_bitop3 truth table 0x42: (s0 ^ s2) & (s1 ^ s2))
 __device__ __forceinline__ bool pair_gen_ok(u32x4 w, uint32_t gen) {
   const uint32_t m = gen - 1u;
-  return (((w[0] ^ m) & (w[1] ^ m) & (w[2] ^ m) & (w[3] ^ m)) & 1u) != 0;
+  uint32_t a, b;
+  asm("v_bitop3_b32 %0, %2, %3, %6 bitop3:0x42\n\tv_bitop3_b32 %1, %4, %5, %6 bitop3:0x42"
+      : "=&v"(a), "=&v"(b)
+      : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "s"(m));
+  return (a & b & 1u) != 0;
 }
 // true when ok holds in every lane of the wave (all lanes are active here)
 __device__ __forceinline__ bool wave_all(bool ok) { return __builtin_amdgcn_ballot_w64(!ok) == 0; }
@@ -518,7 +523,8 @@ __global__ void __launch_bounds__(256, 1)
   const int rho = l >> 2, q = l & 3, orow = 16 * w + rho;
   float m_seg = -INFINITY, lsum = 0.f, m_true = -INFINITY;
   int amax = 0;
-  bool g_valid = false, broken = false;
+  bool g_valid = false;
+  int broken = 0;  // an exchange wait timed out (uniform; an int, not a lane mask)
   u32x4 pf[2] = {z4, z4};
   const int xw = 16 * g + ((r + 4 * g) & 15);
   const int xr = 16 * q + ((rho + 4 * q) & 15);
@@ -721,8 +727,8 @@ __global__ void __launch_bounds__(256, 1)
       pf[1] = Pbuf[h2][32 + m32];
       typedef int i32x4_t __attribute__((ext_vector_type(4)));
       i32x4_t flv = *(const DG_LDS i32x4_t*)flags;  // combined after chunk 0's logit products
-      const bool own_ok = t >= 1 && t - 1 < nt;  // tile t-1 is exchanged
-      const bool sm_ok = t >= 2 && t - 2 < nt;   // tile t-2 gets its softmax
+      const bool own_ok = (uint32_t)(t - 1) < (uint32_t)nt;  // tile t-1 is exchanged
+      const bool sm_ok = (uint32_t)(t - 2) < (uint32_t)nt;   // tile t-2 gets its softmax
       const int v2 = vs + 16 * (sm_ok ? phys(t - 2) : 0);
       DG_LDS u16* tile = (DG_LDS u16*)&Et[t & 3][w][0][0];
       const DG_LDS u16* tpe = (const DG_LDS u16*)&Et[(t + 1) & 3][w][0][0];   // tile t-3
@@ -761,7 +767,8 @@ __global__ void __launch_bounds__(256, 1)
           const uint32_t want = pair_gen(t - 2);
 #pragma unroll
           for (int k = 0; k < Q - 1; ++k) {
-            if (!wave_all(pair_gen_ok(xp[k], want)) && !broken) {
+            if (!wave_all(pair_gen_ok(xp[k], want))) {
+              if (broken) continue;  // a partner already timed out: no more waiting
               if (l == 0) __hip_atomic_fetch_add(&xhdr[9], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               uint32_t xl = xlane;
               asm volatile("" : "+v"(xl));
@@ -770,7 +777,7 @@ __global__ void __launch_bounds__(256, 1)
                 xp[k] = pair_load(xbase, so);
                 if (wave_all(pair_gen_ok(xp[k], want))) break;
                 if (n >= kPairSpin) {
-                  broken = true;
+                  broken = 1;
                   if (l == 0) {
                     __hip_atomic_store(&xhdr[8], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     if (__hip_atomic_fetch_add(&xhdr[10], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
@@ -808,7 +815,7 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[i] = 4 * q + i < lim ? x[i] : -INFINITY;
         }
-        if (c == 4 && j == 3) tm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        if (c == 4 && j == 3) tm = max4_f(x[0], x[1], x[2], x[3]);
         if (c == 4 && j == 4) tm = dpp_max_x1(tm);
         if (c == 4 && j == 5) tm = dpp_max_x2(tm);  // the row's tile max, in all 4 lanes
         if (c == 5 && j == 0 && __any(tm >= m_true)) {
@@ -896,7 +903,7 @@ __global__ void __launch_bounds__(256, 1)
           // the flags' LDS latency hides behind the products above: their
           // first use is pinned after them
           asm volatile("" : "+v"(flv));
-          if (t >= 3 && (flv[0] | flv[1] | flv[2] | flv[3]) != 0) {
+          if (t >= 3 && __builtin_amdgcn_readfirstlane(flv[0] | flv[1] | flv[2] | flv[3]) != 0) {
             // tile t-3's softmax moved a reference: fold the products of the
             // tiles before it under the old one
             fold(acc, 0.f, true);

@@ -125,6 +125,12 @@ __device__ __forceinline__ float dpp_max_x2(float x) {
   asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));
   return r;
 }
+// max of four values in two instructions (never NaN here, as above)
+__device__ __forceinline__ float max4_f(float a, float b, float c, float d) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3\n\tv_max_f32 %0, %0, %4" : "=&v"(r) : "v"(a), "v"(b), "v"(c), "v"(d));
+  return r;
+}
 template <int CTRL>
 __device__ __forceinline__ void argmax_step(float& m, int& a) {
   const float om = dpp_f<CTRL>(m);
