@@ -108,6 +108,7 @@ def test_tiled_embedding_layout(V, d):
     (100, 2048, 5000, "bf16"),                            # CU pairs: ragged 64-row block
     (1, 2048, 200, "bf16"),                               # splits of 2, 1 and 0 tiles
     (130, 2048, 7001, "bf16"),                            # 3 row blocks x 40 splits, ragged ids
+    (300, 2048, 9001, "bf16"),                            # 5 row blocks (the marked layout), ragged rows and ids
     (37, 4096, 3000, "bf16"),                             # 16-row tiles (d = 4096)
 ])
 def test_vocab_matches_oracle(R, d, V, dtype):

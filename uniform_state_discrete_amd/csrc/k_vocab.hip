@@ -427,7 +427,7 @@ __device__ __forceinline__ bool group_handshake(uint32_t* word, int member, uint
   return (v & kGroupSolo) != 0;
 }
 
-template <int Q, bool PIN>
+template <int Q, bool PIN, bool MARK>
 __global__ void __launch_bounds__(256, 1)
     k_vocab_group(const u16* __restrict__ Z, const u16* __restrict__ E, int R, int d, int V, int nrb,
                   int split_len, float* __restrict__ pS, f32x4* __restrict__ pstat,
@@ -719,11 +719,14 @@ __global__ void __launch_bounds__(256, 1)
     };
     const uint32_t xlane = threadIdx.x * 16u;
 
-    // Pairs mark the rare paths (a fold, an exchange poll, a ragged tile, a
+    // MARK marks the rare paths (a fold, an exchange poll, a ragged tile, a
     // new running maximum) unlikely, so that their code moves out of the loop's
-    // straight line: 1.5-3% faster at d = 2048.  Quads keep the default layout:
-    // with the same marks the d = 4096 launch slowed down by 20% and more.
-    constexpr bool kMarkRare = Q == 2;
+    // straight line.  Only pairs over four row blocks or more launch it (2% faster
+    // there).  With two row blocks the same layout made each exchange poll
+    // costly: once the members fell into polling, the launch took 75% longer
+    // (the default layout, in the same state, 10%).  Quads keep the default
+    // layout too: marked, the d = 4096 launch slowed down by 20% and more.
+    constexpr bool kMarkRare = MARK;
     for (int t = 0; t <= nt + 2; ++t) {
       // Tile t-1's partial logits and tile t-3's softmax output (written in
       // the previous iteration) become visible.
@@ -1280,14 +1283,17 @@ hipError_t launch_vocab(const VocabPlan& p, const void* z, const void* E, float*
     uint64_t* xrec = (uint64_t*)(xhdr + kPairHdrWords);
     const uint32_t spin = g_group_spin.load();
     if (p.group == 4)
-      hipLaunchKernelGGL((k_vocab_group<4, false>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb,
-                         p.split_len, pS, pstat, xhdr, xrec, spin);
+      hipLaunchKernelGGL((k_vocab_group<4, false, false>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V,
+                         p.nrb, p.split_len, pS, pstat, xhdr, xrec, spin);
     else if (p.nrb == 1)  // at most 64 rows
-      hipLaunchKernelGGL((k_vocab_group<2, true>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb,
-                         p.split_len, pS, pstat, xhdr, xrec, spin);
+      hipLaunchKernelGGL((k_vocab_group<2, true, false>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V,
+                         p.nrb, p.split_len, pS, pstat, xhdr, xrec, spin);
+    else if (p.nrb < 4)  // 65 to 192 rows
+      hipLaunchKernelGGL((k_vocab_group<2, false, false>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V,
+                         p.nrb, p.split_len, pS, pstat, xhdr, xrec, spin);
     else
-      hipLaunchKernelGGL((k_vocab_group<2, false>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb,
-                         p.split_len, pS, pstat, xhdr, xrec, spin);
+      hipLaunchKernelGGL((k_vocab_group<2, false, true>), pgrid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V,
+                         p.nrb, p.split_len, pS, pstat, xhdr, xrec, spin);
   } else if (p.variant == 1) {
     switch (sl) {
       case 32: hipLaunchKernelGGL(k_vocab32<32>, grid, dim3(256), 0, s, Zb, Eb, p.rows, p.d, p.V, p.nrb, p.split_len, pS, pstat); break;
