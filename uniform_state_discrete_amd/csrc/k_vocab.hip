@@ -727,6 +727,32 @@ __global__ void __launch_bounds__(256, 1)
     // (the default layout, in the same state, 10%).  Quads keep the default
     // layout too: marked, the d = 4096 launch slowed down by 20% and more.
     constexpr bool kMarkRare = MARK;
+    // A late partner record is waited for in a poll loop whose every reload
+    // also waits for the E loads issued before it (vector loads complete in
+    // order).  With one row block E comes straight from HBM and that wait is
+    // most of a tile: the waiting member falls behind by more than the
+    // exchange margin, its partner then finds a late record in turn, and the
+    // pair keeps alternating (about 16% of waits poll, 385 us at 1-64 rows).
+    // kDefer re-loads a late record in chunk 4 and waits for it only at the
+    // start of chunk 7, where the loads issued before it are 3-4 chunks old,
+    // and runs the skipped softmax steps there: 285-305 us, 5% of waits late.
+    // Launches with several row blocks read E mostly from L2, where a wait
+    // is short, and keep the plain loop.
+    constexpr bool kDefer = PIN;
+    bool defer = false;  // uniform: a late record's softmax steps wait for chunk 7
+    // a wait that hit its bound: raise the error flag, record the first one
+    auto exchange_timeout = [&](int k, int t) {
+      broken = 1;
+      if (l == 0) {
+        __hip_atomic_store(&xhdr[8], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__hip_atomic_fetch_add(&xhdr[10], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+          xhdr[12] = (uint32_t)grp;
+          xhdr[13] = (uint32_t)t;
+          xhdr[14] = (uint32_t)(mb | (w << 4));
+          xhdr[15] = xp[k][0] & 1u;
+        }
+      }
+    };
     for (int t = 0; t <= nt + 2; ++t) {
       // Tile t-1's partial logits and tile t-3's softmax output (written in
       // the previous iteration) become visible.
@@ -755,6 +781,7 @@ __global__ void __launch_bounds__(256, 1)
       // block, where streaming E dominates: 10-16% at 1 row).  The chunks
       // themselves stay in order either way.
       auto stage = [&](int c, int j) {
+        const bool live = !(kDefer && defer);  // false: this tile's softmax steps run in chunk 7
         if (c == 2 && j == 0) {
 #pragma unroll
           for (int s4 = 0; s4 < 4; ++s4) xa[s4] = xch[s4][w][xr];
@@ -782,27 +809,23 @@ __global__ void __launch_bounds__(256, 1)
               uint32_t xl = xlane;
               asm volatile("" : "+v"(xl));
               const uint32_t so = xo_in(k) + ((t - 2) & 3) * 4096u + xl;
+              if constexpr (kDefer) {
+                xp[k] = pair_load(xbase, so);  // waited for in chunk 7
+                defer = true;
+                continue;
+              }
               for (uint32_t n = 0;; ++n) {
                 xp[k] = pair_load(xbase, so);
                 if (wave_all(pair_gen_ok(xp[k], want))) break;
                 if (n >= kPairSpin) {
-                  broken = 1;
-                  if (l == 0) {
-                    __hip_atomic_store(&xhdr[8], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (__hip_atomic_fetch_add(&xhdr[10], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-                      xhdr[12] = (uint32_t)grp;
-                      xhdr[13] = (uint32_t)t;
-                      xhdr[14] = (uint32_t)(mb | (w << 4));
-                      xhdr[15] = xp[k][0] & 1u;
-                    }
-                  }
+                  exchange_timeout(k, t);
                   break;
                 }
               }
             }
           }
         }
-        if (c == 4 && j == 1) {
+        if (c == 4 && j == 1 && live) {
           // every member adds the Q partials in member order (for two members
           // own + other is that sum: the addition commutes exactly)
 #pragma unroll
@@ -818,17 +841,17 @@ __global__ void __launch_bounds__(256, 1)
             }
           }
         }
-        if (c == 4 && j == 2 &&
+        if (c == 4 && j == 2 && live &&
             (kMarkRare ? __builtin_expect(!(sm_ok && v2 + 16 <= ve), 0) : !(sm_ok && v2 + 16 <= ve))) {
           // a ragged or absent tile (uniform): ids past the split are -inf
           const int lim = sm_ok ? ve - v2 : 0;
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[i] = 4 * q + i < lim ? x[i] : -INFINITY;
         }
-        if (c == 4 && j == 3) tm = max4_f(x[0], x[1], x[2], x[3]);
-        if (c == 4 && j == 4) tm = dpp_max_x1(tm);
-        if (c == 4 && j == 5) tm = dpp_max_x2(tm);  // the row's tile max, in all 4 lanes
-        if (c == 5 && j == 0 && (kMarkRare ? __builtin_expect(__any(tm >= m_true), 0) : __any(tm >= m_true))) {
+        if (c == 4 && j == 3 && live) tm = max4_f(x[0], x[1], x[2], x[3]);
+        if (c == 4 && j == 4 && live) tm = dpp_max_x1(tm);
+        if (c == 4 && j == 5 && live) tm = dpp_max_x2(tm);  // the row's tile max, in all 4 lanes
+        if (c == 5 && j == 0 && live && (kMarkRare ? __builtin_expect(__any(tm >= m_true), 0) : __any(tm >= m_true))) {
           // the running max may move (uniform branch, rare after a split's
           // first tiles): lowest id attaining the tile max; tiles come out of
           // id order, so a tie goes to the lower id.  The offset within the
@@ -843,36 +866,36 @@ __global__ void __launch_bounds__(256, 1)
           amax = better ? cand : amax;
           m_true = fmaxf(m_true, tm);
         }
-        if (c == 5 && j == 1) {
+        if (c == 5 && j == 1 && live) {
           // Lazy reference: it only moves when a logit exceeds it by more than
           // kLazyTh; the running sum is then rescaled by s = e^(m_old - m_new).
           first = m_seg == -INFINITY;
           over = !first & (tm > m_seg + kLazyTh);
           s = over ? __builtin_amdgcn_exp2f((m_seg - tm) * kLog2e) : 1.f;
         }
-        if (c == 5 && j == 2) {
+        if (c == 5 && j == 2 && live) {
           m_seg = (first | over) ? tm : m_seg;
           ms = m_seg == -INFINITY ? 0.f : m_seg;  // a row with no valid logit yet: all p are 0
         }
         // p = 2^((x - m) log2 e): exact 1 at the maximum, 0 for a masked -inf;
         // results below 2^-126 flush to 0 (more than 87 below the reference)
-        if (c == 5 && j == 3) {
+        if (c == 5 && j == 3 && live) {
           x[0] = __builtin_amdgcn_exp2f((x[0] - ms) * kLog2e);
           x[1] = __builtin_amdgcn_exp2f((x[1] - ms) * kLog2e);
         }
-        if (c == 5 && j == 4) {
+        if (c == 5 && j == 4 && live) {
           x[2] = __builtin_amdgcn_exp2f((x[2] - ms) * kLog2e);
           x[3] = __builtin_amdgcn_exp2f((x[3] - ms) * kLog2e);
         }
-        if (c == 5 && j == 5) lsum = fmaf(lsum, s, (x[0] + x[1]) + (x[2] + x[3]));
-        if (c == 6 && j == 0) {
+        if (c == 5 && j == 5 && live) lsum = fmaf(lsum, s, (x[0] + x[1]) + (x[2] + x[3]));
+        if (c == 6 && j == 0 && live) {
           typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
           typedef float f32x2v __attribute__((ext_vector_type(2)));
           const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x[0], x[1]}, bf16x2v));
           const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x[2], x[3]}, bf16x2v));
           *(DG_LDS u32x2*)((DG_LDS char*)&Pbuf[q >> 1][orow] + 8 * (q & 1)) = u32x2{lo, hi};
         }
-        if (c == 6 && j == 1) {
+        if (c == 6 && j == 1 && live) {
           // every lane of a row writes the same factor, every lane of the wave
           // the same flag (no branch; orow = threadIdx.x / 4)
           Sbuf[threadIdx.x >> 2] = s;
@@ -888,6 +911,31 @@ __global__ void __launch_bounds__(256, 1)
           for (int h = 0; h < 4; ++h) xch[w][h][xw] = lg[h];
         }
         *(DG_LDS u32x4*)(tile + wr + 512 * c) = e;
+        if (kDefer && c == 7 && defer) {
+          // the late record of tile t-2, re-loaded in chunk 4: wait for it
+          // here, then run the softmax steps skipped in chunks 4-6
+          const uint32_t want = pair_gen(t - 2);
+          uint32_t xl = xlane;
+          asm volatile("" : "+v"(xl));
+#pragma unroll
+          for (int k = 0; k < Q - 1; ++k) {
+            const uint32_t so = xo_in(k) + ((t - 2) & 3) * 4096u + xl;
+            for (uint32_t n = 0; !broken && !wave_all(pair_gen_ok(xp[k], want)); ++n) {
+              if (n >= kPairSpin) {
+                exchange_timeout(k, t);
+                break;
+              }
+              xp[k] = pair_load(xbase, so);
+            }
+          }
+          defer = false;
+#pragma unroll
+          for (int jj = 1; jj < 6; ++jj) stage(4, jj);
+#pragma unroll
+          for (int jj = 0; jj < 6; ++jj) stage(5, jj);
+          stage(6, 0);
+          stage(6, 1);
+        }
         if (c == 7 && own_ok) {
           // the other members' partials of tile t-1 (stored at chunk 3 of
           // this iteration), consumed at chunk 4 of the next; the lane offset
