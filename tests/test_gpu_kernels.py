@@ -312,6 +312,10 @@ def _run_attn(B, C, L, cap, Hq, Hkv, dh, dtype, arrs, causal):
     # causal, GQA 3: row blocks 0-1 fit one split (written directly), row
     # block 2 is split; position 85 has rows in both kinds of row block
     (1, 100, 40, 6, 2, 64, "bf16", 1.0),
+    # caches of whole 64-key tiles: the three-tile ring when not causal
+    (2, 37, 128, 4, 2, 64, "bf16", 1.0),       # two cache tiles, then a ragged canvas tile
+    (1, 16, 2048, 8, 2, 128, "bf16", 2.0),     # 17 splits of two tiles (many-splits combine)
+    (3, 100, 192, 6, 2, 64, "bf16", 1.0),      # a split that runs from cache tiles into canvas tiles
 ])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_attention_matches_oracle(B, C, L, Hq, Hkv, dh, dtype, qscale, causal):

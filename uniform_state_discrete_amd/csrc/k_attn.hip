@@ -26,6 +26,10 @@ namespace dg {
 // K/V tiles of 64 keys are double-buffered in LDS through registers; one
 // barrier per tile.  Rows of the K tile are padded by 16 B and of the V tile
 // by 64 B so that the row-wise and the transposing reads are conflict-free.
+// KSPLIT (launches of at most 64 packed rows): waves w and w + 2 take the same
+// 32 rows and the two 32-key halves of every tile, so all four SIMDs work
+// (otherwise waves 2 and 3 only move tiles); the halves merge their running
+// max, sum and accumulators through LDS after the last tile.
 // ---------------------------------------------------------------------------
 constexpr float kAttnLazy = 8.0f;
 
@@ -40,7 +44,7 @@ __host__ __device__ inline int attn_key_limit(int causal, int L, int C, int G, i
   return lim < nkeys ? lim : nkeys;
 }
 
-template <int DH>
+template <int DH, bool KSPLIT>
 __global__ void __launch_bounds__(256, 2)
     k_attn_bf16(int B, int C, int L, int cap, int Hq, int Hkv, int G, int causal, int nrb,
                 int nsplit, int kps, const u16* __restrict__ Q, const u16* __restrict__ Kc,
@@ -76,9 +80,12 @@ __global__ void __launch_bounds__(256, 2)
   if (direct && split > 0) return;
   const int k_begin = split * kps;
   const int k_end = min(k_lim, k_begin + kps);
-  const int row = rb * 128 + w * 32 + l32;
+  const int wr = KSPLIT ? (w & 1) : w;  // this wave's group of 32 packed rows
+  const int kh = KSPLIT ? (w >> 1) : 0;  // KSPLIT: this wave's 32-key half of each tile
+  constexpr int NKB = KSPLIT ? 1 : 2;    // 32-key chains of S^T per wave
+  const int row = rb * 128 + wr * 32 + l32;
   const bool rok = row < M;
-  const bool wave_live = rb * 128 + w * 32 < M;  // uniform over the wave
+  const bool wave_live = rb * 128 + wr * 32 < M;  // uniform over the wave
   const int qi = rok ? row / G : 0, qh = g * G + (rok ? row % G : 0);
   const u32x4 z4 = {0u, 0u, 0u, 0u};
 
@@ -172,12 +179,15 @@ __global__ void __launch_bounds__(256, 2)
     if (wave_live) {
       // S^T for keys 0..31 and 32..63: two independent chains interleaved, K
       // fragments read two steps ahead of their products
-      f32x16 sacc[2] = {zero16(), zero16()};
+      f32x16 sacc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = zero16();
       {
-        u32x4 ka[3][2];
+        u32x4 ka[3][NKB];
         auto kread = [&](int ks) {
   #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) ka[ks % 3][kb] = *(const u32x4*)&Ks[buf][kb * 32 + l32][ks * 16 + h * 8];
+          for (int kb = 0; kb < NKB; ++kb)
+            ka[ks % 3][kb] = *(const u32x4*)&Ks[buf][(kh + kb) * 32 + l32][ks * 16 + h * 8];
         };
         kread(0);
         kread(1);
@@ -185,7 +195,7 @@ __global__ void __launch_bounds__(256, 2)
         for (int ks = 0; ks < KS; ++ks) {
           if (ks + 2 < KS) kread(ks + 2);
   #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(ka[ks % 3][kb], qf[ks], sacc[kb]);
+          for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma32(ka[ks % 3][kb], qf[ks], sacc[kb]);
         }
       }
       // scores stay unscaled: p = 2^(s sl2 - m) with m in the scaled (log2) domain
@@ -193,17 +203,17 @@ __global__ void __launch_bounds__(256, 2)
         // a ragged tile or one that crosses the causal diagonal (uniform
         // branch): masked keys get -inf
   #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
   #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int key = t0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+            const int key = t0 + (kh + kb) * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
             const bool valid = key < k_end && (!causal || key <= qlim);
             sacc[kb][e] = valid ? sacc[kb][e] : -INFINITY;
           }
       }
       float tmax = -INFINITY;
   #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
   #pragma unroll
         for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(sacc[kb][e], sacc[kb][e + 1]));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;  // sl2 > 0 keeps the order
@@ -222,9 +232,10 @@ __global__ void __launch_bounds__(256, 2)
       typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
       typedef float f32x2v __attribute__((ext_vector_type(2)));
       const bf16x2v one2 = __builtin_bit_cast(bf16x2v, 0x3f803f80u);  // (1, 1)
-      u32x4 pf[4];
+      constexpr int NQ = 2 * NKB;  // 16-key groups of this wave's keys
+      u32x4 pf[NQ];
   #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         uint32_t pk[4];
   #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -246,7 +257,7 @@ __global__ void __launch_bounds__(256, 2)
         auto vread = [&](int q) {
   #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            const int r0 = 16 * q + 4 * h + ((l & 15) >> 2);
+            const int r0 = 32 * kh + 16 * q + 4 * h + ((l & 15) >> 2);
             const int c0 = mb * 32 + 16 * ((l >> 4) & 1) + (l & 3) * 4;
             const u32x2 a0 = lds_read_tr16(vbase + r0 * VP + c0);
             const u32x2 a1 = lds_read_tr16(vbase + (r0 + 8) * VP + c0);
@@ -255,8 +266,8 @@ __global__ void __launch_bounds__(256, 2)
         };
         vread(0);
   #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (q + 1 < 4) vread(q + 1);
+        for (int q = 0; q < NQ; ++q) {
+          if (q + 1 < NQ) vread(q + 1);
   #pragma unroll
           for (int mb = 0; mb < MB; ++mb) oacc[mb] = mfma32(va[q & 1][mb], pf[q], oacc[mb]);
         }
@@ -266,6 +277,35 @@ __global__ void __launch_bounds__(256, 2)
     __syncthreads();
   }
   lsum += __shfl_xor(lsum, 32);
+  if constexpr (KSPLIT) {
+    // Wave w + 2 hands its reference, sum and accumulators (in its own lane
+    // layout) to wave w through the K buffers, free after the last tile's
+    // barrier; wave w merges them under the larger reference.
+    constexpr int NX = MB * 16 + 2;  // floats per lane
+    float* xs = (float*)&Ks[0][0][0] + (size_t)wr * NX * 64 + l;
+    if (kh == 1 && wave_live) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xs[(mb * 16 + i) * 64] = oacc[mb][i];
+      xs[(MB * 16) * 64] = m;
+      xs[(MB * 16 + 1) * 64] = lsum;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    if (wave_live) {
+      const float m2 = xs[(MB * 16) * 64], l2 = xs[(MB * 16 + 1) * 64];
+      const float mn = fmaxf(m, m2);
+      const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+      const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[mb][i] = oacc[mb][i] * a + xs[(mb * 16 + i) * 64] * a2;
+      lsum = lsum * a + l2 * a2;
+      m = mn;
+    }
+  }
   if (!rok) return;
   const size_t orow = ((size_t)b * C + qi) * Hq + qh;
   if (direct) {
@@ -593,15 +633,20 @@ hipError_t launch_attn(const AttnPlan& p, const void* q, const void* kc, const v
   float* mpart = Opart + (size_t)p.nsplit * nrows * p.dh;
   float* lpart = mpart + (size_t)p.nsplit * nrows;
   const dim3 grid((unsigned)((p.nrb * p.nsplit * p.Hkv * p.B + 7) / 8 * 8));
-#define DG_ATTN_LAUNCH(DHV)                                                                       \
-  hipLaunchKernelGGL(k_attn_bf16<DHV>, grid, dim3(256), 0, s, p.B, p.C, p.L, p.cap, p.Hq, p.Hkv, \
+  const bool ksplit = p.C * G <= 64;  // one row block with at most two row groups
+#define DG_ATTN_LAUNCH(DHV, KSPLITV)                                                              \
+  hipLaunchKernelGGL((k_attn_bf16<DHV, KSPLITV>), grid, dim3(256), 0, s, p.B, p.C, p.L, p.cap, p.Hq, p.Hkv, \
                      G, p.causal, p.nrb, p.nsplit, p.keys_per_split, (const u16*)q,                \
                      (const u16*)kc, (const u16*)vc, (const u16*)kn, (const u16*)vn, (u16*)out,    \
                      lse, Opart, mpart, lpart)
-  if (p.dh == 128)
-    DG_ATTN_LAUNCH(128);
+  if (p.dh == 128 && ksplit)
+    DG_ATTN_LAUNCH(128, true);
+  else if (p.dh == 128)
+    DG_ATTN_LAUNCH(128, false);
+  else if (ksplit)
+    DG_ATTN_LAUNCH(64, true);
   else
-    DG_ATTN_LAUNCH(64);
+    DG_ATTN_LAUNCH(64, false);
 #undef DG_ATTN_LAUNCH
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev_end) e = hipEventRecord(ev_end, s);
