@@ -721,7 +721,7 @@ __global__ void __launch_bounds__(256, 1)
 
     // MARK marks the rare paths (a fold, an exchange poll, a ragged tile, a
     // new running maximum) unlikely, so that their code moves out of the loop's
-    // straight line.  Only pairs over four row blocks or more launch it (2% faster
+    // straight line.  Only pair launches of four row blocks or more use it (2% faster
     // there).  With two row blocks the same layout made each exchange poll
     // costly: once the members fell into polling, the launch took 75% longer
     // (the default layout, in the same state, 10%).  Quads keep the default
@@ -735,7 +735,7 @@ __global__ void __launch_bounds__(256, 1)
     // pair keeps alternating (about 16% of waits poll, 385 us at 1-64 rows).
     // kDefer re-loads a late record in chunk 4 and waits for it only at the
     // start of chunk 7, where the loads issued before it are 3-4 chunks old,
-    // and runs the skipped softmax steps there: 285-305 us, 5% of waits late.
+    // and runs the skipped softmax steps there: 281-318 us, 5% of waits late.
     // Launches with several row blocks read E mostly from L2, where a wait
     // is short, and keep the plain loop.
     constexpr bool kDefer = PIN;
