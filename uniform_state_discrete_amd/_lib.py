@@ -12,7 +12,10 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdg.so")
+# DG_LIB names another build of the same library (for example the host-side
+# AddressSanitizer build of `python -m uniform_state_discrete_amd.build
+# --host-asan PATH`); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("DG_LIB") or os.path.join(HERE, "libdg.so")
 
 DG_F32, DG_BF16 = 0, 1
 DG_OK, DG_EINVAL, DG_EUNSUPPORTED, DG_EWORKSPACE, DG_EHIP = 0, -1, -2, -3, -4

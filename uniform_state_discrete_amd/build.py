@@ -57,15 +57,28 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+# Host-side AddressSanitizer (the device code is compiled as usual): every
+# sanitizer flag applies to the host pass only.
+HOST_ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+                   "-Xarch_host", "-g"]
+
+
+def build(verbose=False, host_asan=None):
+    """Compile every source for gfx950 and link libdg.so in the package.
+    host_asan: a path; then the host code is built with AddressSanitizer
+    into that library instead (load it through DG_LIB, with the clang
+    AddressSanitizer runtime preloaded, to run the CPU tests under it)."""
+    bdir = BUILD if host_asan is None else BUILD + "_host_asan"
+    os.makedirs(bdir, exist_ok=True)
     hipcc = _hipcc()
+    extra = [] if host_asan is None else HOST_ASAN_FLAGS
     objs = []
     cmds = []
     for src in sources():
-        obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+        obj = os.path.join(bdir, os.path.basename(src)[:-4] + ".o")
         objs.append(obj)
-        cmds.append([hipcc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj])
+        cmds.append([hipcc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src,
+                     "-o", obj])
 
     def run(cmd):
         if verbose:
@@ -80,17 +93,23 @@ def build(verbose=False):
             if verbose and err.strip():
                 print(err)
     tl = torch_lib_dir()
-    tmp = LIB + ".tmp"
-    link = ["g++", "-shared", "-o", tmp, *objs, f"-L{tl}", "-l:libamdhip64.so",
-            f"-Wl,-rpath,{tl}", "-Wl,--no-undefined"]
+    out = LIB if host_asan is None else os.path.abspath(host_asan)
+    tmp = out + ".tmp"
+    if host_asan is None:
+        link = ["g++", "-shared", "-o", tmp, *objs, f"-L{tl}", "-l:libamdhip64.so",
+                f"-Wl,-rpath,{tl}", "-Wl,--no-undefined"]
+    else:  # the sanitizer runtime is clang's, shared, preloaded by the caller
+        link = [hipcc, "-shared", "-Xarch_host", "-fsanitize=address", "-shared-libsan", "-o", tmp, *objs,
+                f"-L{tl}", "-l:libamdhip64.so", f"-Wl,-rpath,{tl}"]
     if verbose:
         print(" ".join(link), flush=True)
     r = subprocess.run(link, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(link)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    asan = sys.argv[sys.argv.index("--host-asan") + 1] if "--host-asan" in sys.argv else None
+    print(build(verbose="--verbose" in sys.argv, host_asan=asan))
