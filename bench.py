@@ -25,15 +25,18 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 DEFAULT_WORKLOAD = "canvas256_L8192_d2048_V262144"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_vocab_traffic.json")
 VOCAB_SOURCES = [os.path.join(ROOT, "uniform_state_discrete_amd", "csrc", f)
-                 for f in ("k_vocab.hip", "vocab_common.h", "dg_common.h")] + [
-    os.path.join(ROOT, "uniform_state_discrete_amd", "build.py")]  # its flags shape the code
+                 for f in ("k_vocab.hip", "vocab_common.h", "dg_common.h")]
 
 
 def vocab_source_hash():
+    """SHA-256 of the vocabulary kernel's sources and of the compile flags
+    that shape its code (so a traffic record holds only for that code)."""
+    from uniform_state_discrete_amd import build as B
     h = hashlib.sha256()
     for p in VOCAB_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
+    h.update(json.dumps([B.HIPCC_FLAGS, B.SOURCE_FLAGS.get("k_vocab.hip", [])]).encode())
     return h.hexdigest()
 
 
