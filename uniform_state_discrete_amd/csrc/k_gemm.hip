@@ -5,18 +5,21 @@
 
 namespace dg {
 
-// bf16 path.  Workgroup = 4 waves, output tile 64 (m) x 64 (n), wave tile
-// 32 x 32.  K advances in slices of 64 staged through LDS (double-buffered):
-// 8 threads load one 128-byte row segment with 16-byte loads, so every global
-// load instruction reads whole contiguous rows; global loads run four slices
-// (64 KiB per workgroup) ahead of the products, enough bytes in flight to
-// cover the latency of the weight stream from HBM.  Computed as C^T = B . A^T on 32x32x16 MFMA tiles
-// (A operand: weight rows, B operand: activation rows, both read from LDS
-// with one 16-byte read per lane), so each lane ends up holding 4 consecutive
-// output columns of one output row (8-byte stores).  Two accumulators take
-// alternate K-steps: two independent chains keep the matrix core busy.
-// Up to three (weight, output) segments share one launch (the Q, K and V
-// projections read the same activations).
+// bf16 path.  Output tile TM (m) x 64 (n), wave tile 32 x 32: 4 waves for
+// TM = 64; 2 waves for TM = 32, which the host picks when 64-row tiles would
+// leave CUs without a workgroup (256 rows of a 2048-wide output: 128 tiles
+// of 64 x 64; 32-row tiles give 256 workgroups, 12.2 against 13.9 us).
+// K advances in slices of 64 staged through LDS (double-buffered): 8 threads
+// load one 128-byte row segment with 16-byte loads, so every global load
+// instruction reads whole contiguous rows; global loads run four slices
+// (64 or 48 KiB per workgroup) ahead of the products, enough bytes in flight
+// to cover the latency of the weight stream from HBM.  Computed as
+// C^T = B . A^T on 32x32x16 MFMA tiles (A operand: weight rows, B operand:
+// activation rows, both read from LDS with one 16-byte read per lane), so
+// each lane ends up holding 4 consecutive output columns of one output row
+// (8-byte stores).  Two accumulators take alternate K-steps: two independent
+// chains keep the matrix core busy.  Up to three (weight, output) segments
+// share one launch (the Q, K and V projections read the same activations).
 constexpr int GKS = 64, GLD = GKS + 8;  // K slice; LDS row of 144 bytes: conflict-free
 
 // The cache copy of output element(s) of row am, columns n .. n+cnt-1 (within
@@ -29,16 +32,20 @@ __device__ __forceinline__ u16* cache_row(u16* cache, const CacheGeom& cg, int N
   return cache + (((size_t)b * (N / cg.dh) + g) * cg.cap + cg.L + i) * cg.dh + e;
 }
 
-__global__ void __launch_bounds__(256) k_gemm_nt_bf16(int M, int K, const u16* __restrict__ A, GemmSeg s0,
-                                                      GemmSeg s1, GemmSeg s2, u32x4* __restrict__ zp,
-                                                      size_t zn16, CacheGeom cg) {
+template <int TM>
+__global__ void __launch_bounds__(TM * 4) k_gemm_nt_bf16(int M, int K, const u16* __restrict__ A, GemmSeg s0,
+                                                         GemmSeg s1, GemmSeg s2, u32x4* __restrict__ zp,
+                                                         size_t zn16, CacheGeom cg) {
+  static_assert(TM == 64 || TM == 32, "row tile of 64 (4 waves) or 32 (2 waves)");
+  constexpr int RS = TM / 2;                 // rows per loader pass: 8 threads per 128-byte row segment
+  constexpr int JA = TM / RS, JB = 64 / RS;  // loader passes over the A and B tiles
   if (zp) {
     // a region a later kernel needs zeroed, spread over every thread of the grid
     const size_t nth = (size_t)gridDim.x * gridDim.y * blockDim.x;
     for (size_t i = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; i < zn16; i += nth)
       zp[i] = u32x4{0u, 0u, 0u, 0u};
   }
-  __shared__ __attribute__((aligned(16))) u16 As[2][64][GLD];
+  __shared__ __attribute__((aligned(16))) u16 As[2][TM][GLD];
   __shared__ __attribute__((aligned(16))) u16 Bs[2][64][GLD];
   int tile = blockIdx.x;
   GemmSeg sg = s0;
@@ -52,9 +59,9 @@ __global__ void __launch_bounds__(256) k_gemm_nt_bf16(int M, int K, const u16* _
   }
   const int N = sg.N;
   const u16* __restrict__ B = sg.B;
-  const int m0 = blockIdx.y * 64, n0 = tile * 64;
+  const int m0 = blockIdx.y * TM, n0 = tile * 64;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
-  const int lr = tid >> 3, lc = (tid & 7) * 8;  // loader: rows lr, lr + 32; columns lc .. lc+7
+  const int lr = tid >> 3, lc = (tid & 7) * 8;  // loader: rows lr + RS j; columns lc .. lc+7
   const int nk = K / GKS;                       // K is a multiple of 64
   // Buffer resources end at the operands: rows past M or N load zeros, with
   // no branch around the loads.
@@ -63,26 +70,26 @@ __global__ void __launch_bounds__(256) k_gemm_nt_bf16(int M, int K, const u16* _
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(B), (short)0,
                                                                       (int)((size_t)N * K * 2), 0x00020000);
   const uint32_t oa = (uint32_t)(((size_t)(m0 + lr) * K + lc) * 2), ob = (uint32_t)(((size_t)(n0 + lr) * K + lc) * 2);
-  const uint32_t row32 = (uint32_t)(32 * K * 2);
-  constexpr int GPF = 4;         // slices in flight
-  u32x4 ga[GPF][2], gb[GPF][2];  // [slot][row half]
+  const uint32_t rowRS = (uint32_t)(RS * K * 2);
+  constexpr int GPF = 4;           // slices in flight
+  u32x4 ga[GPF][JA], gb[GPF][JB];  // [slot][loader pass]
   auto gload = [&](int slot, int ks) {
     const uint32_t k2 = (uint32_t)(ks * GKS * 2);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      ga[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, oa + j * row32 + k2, 0, 0));
-      gb[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob + j * row32 + k2, 0, 0));
-    }
+    for (int j = 0; j < JA; ++j)
+      ga[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, oa + j * rowRS + k2, 0, 0));
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+      gb[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob + j * rowRS + k2, 0, 0));
   };
   auto lstore = [&](int slot, int buf) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      *(DG_LDS u32x4*)&As[buf][lr + 32 * j][lc] = ga[slot][j];
-      *(DG_LDS u32x4*)&Bs[buf][lr + 32 * j][lc] = gb[slot][j];
-    }
+    for (int j = 0; j < JA; ++j) *(DG_LDS u32x4*)&As[buf][lr + RS * j][lc] = ga[slot][j];
+#pragma unroll
+    for (int j = 0; j < JB; ++j) *(DG_LDS u32x4*)&Bs[buf][lr + RS * j][lc] = gb[slot][j];
   };
   f32x16 acc0 = zero16(), acc1 = zero16();
-  const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
+  const int wm = TM == 64 ? (w >> 1) * 32 : 0, wn = TM == 64 ? (w & 1) * 32 : w * 32;
 #pragma unroll
   for (int s = 0; s < GPF; ++s) gload(s, s);
   lstore(0, 0);
@@ -298,6 +305,23 @@ __global__ void __launch_bounds__(256) k_gemm_nt_f32(int M, int N, int K, const 
 
 // Row count from which the 128 x 128 tile kernel runs.
 constexpr int kGemmBigM = 1024;
+// Below it, 64 x 64 tiles unless they leave CUs of an MI355X (256) without a
+// workgroup: then 32 x 64 tiles with two waves each.
+constexpr int kGemmFill = 256;
+
+static hipError_t launch_gemm_small(int M, int K, const void* A, const GemmSeg& s0, const GemmSeg& s1,
+                                    const GemmSeg& s2, void* zero, size_t zero_bytes, const CacheGeom& cg,
+                                    hipStream_t s) {
+  const int tiles = s0.tiles + s1.tiles + s2.tiles;
+  if ((size_t)tiles * (size_t)((M + 63) / 64) >= (size_t)kGemmFill) {
+    hipLaunchKernelGGL(k_gemm_nt_bf16<64>, dim3((unsigned)tiles, (M + 63) / 64), dim3(256), 0, s, M, K,
+                       (const u16*)A, s0, s1, s2, (u32x4*)zero, zero_bytes / 16, cg);
+  } else {
+    hipLaunchKernelGGL(k_gemm_nt_bf16<32>, dim3((unsigned)tiles, (M + 31) / 32), dim3(128), 0, s, M, K,
+                       (const u16*)A, s0, s1, s2, (u32x4*)zero, zero_bytes / 16, cg);
+  }
+  return hipGetLastError();
+}
 
 static GemmSeg gemm_seg(const void* B, const void* Res, void* C, int N, int tn, void* cache = nullptr) {
   return GemmSeg{(const u16*)B, (const u16*)Res, (u16*)C, N, (N + tn - 1) / tn, (u16*)cache};
@@ -310,13 +334,10 @@ hipError_t launch_gemm_nt(int dtype, int M, int N, int K, const void* A, const v
     const int tn = M >= kGemmBigM ? 128 : 64;
     const GemmSeg s0 = gemm_seg(B, Res, C, N, tn), none = GemmSeg{nullptr, nullptr, nullptr, 0, 0, nullptr};
     const CacheGeom cg{1, 0, 1, 1};
+    if (tn != 128) return launch_gemm_small(M, K, A, s0, none, none, zero, zero_bytes, cg, s);
     dim3 grid((unsigned)s0.tiles, (M + tn - 1) / tn);
-    if (tn == 128)
-      hipLaunchKernelGGL(k_gemm_nt_bf16_t128, grid, dim3(256), 0, s, M, K, (const u16*)A, s0, none, none,
-                         (u32x4*)zero, zero_bytes / 16, cg);
-    else
-      hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, s0, none, none, (u32x4*)zero,
-                         zero_bytes / 16, cg);
+    hipLaunchKernelGGL(k_gemm_nt_bf16_t128, grid, dim3(256), 0, s, M, K, (const u16*)A, s0, none, none,
+                       (u32x4*)zero, zero_bytes / 16, cg);
   } else {
     dim3 grid((N + 15) / 16, (M + 15) / 16);
     hipLaunchKernelGGL(k_gemm_nt_f32, grid, dim3(256), 0, s, M, N, K, (const float*)A,
@@ -342,13 +363,10 @@ hipError_t launch_gemm_qkv(int dtype, int M, int K, const void* A, const void* W
   const int tn = M >= kGemmBigM ? 128 : 64;
   const GemmSeg sq = gemm_seg(Wq, nullptr, Q, Nq, tn), sk = gemm_seg(Wk, nullptr, Kn, Nkv, tn, k_cache),
                 sv = gemm_seg(Wv, nullptr, Vn, Nkv, tn, v_cache);
+  if (tn != 128) return launch_gemm_small(M, K, A, sq, sk, sv, nullptr, 0, g, s);
   dim3 grid((unsigned)(sq.tiles + sk.tiles + sv.tiles), (M + tn - 1) / tn);
-  if (tn == 128)
-    hipLaunchKernelGGL(k_gemm_nt_bf16_t128, grid, dim3(256), 0, s, M, K, (const u16*)A, sq, sk, sv, nullptr,
-                       (size_t)0, g);
-  else
-    hipLaunchKernelGGL(k_gemm_nt_bf16, grid, dim3(256), 0, s, M, K, (const u16*)A, sq, sk, sv, nullptr, (size_t)0,
-                       g);
+  hipLaunchKernelGGL(k_gemm_nt_bf16_t128, grid, dim3(256), 0, s, M, K, (const u16*)A, sq, sk, sv, nullptr,
+                     (size_t)0, g);
   return hipGetLastError();
 }
 
