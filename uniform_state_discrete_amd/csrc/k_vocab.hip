@@ -727,6 +727,12 @@ __global__ void __launch_bounds__(256, 1)
     // (the default layout, in the same state, 10%).  Quads keep the default
     // layout too: marked, the d = 4096 launch slowed down by 20% and more.
     constexpr bool kMarkRare = MARK;
+    // The same instances store chunk 0's partial logits one row group at a
+    // time, each just before the product that overwrites it, instead of all
+    // four (and the E chunk) ahead of the products: the products start while
+    // the stores drain.  1% faster at 256 rows (0.596-0.603 against
+    // 0.606-0.611 ms), 2% at V = 32768; the quads fell into polling with it.
+    constexpr bool kC0Interleave = MARK;
     // A late partner record is waited for in a poll loop whose every reload
     // also waits for the E loads issued before it (vector loads complete in
     // order).  With one row block E comes straight from HBM and that wait is
@@ -905,12 +911,12 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const u32x4 e = ring[c % PF];
-        if (c == 0) {
+        if (c == 0 && !kC0Interleave) {
           // tile t-1's partial logits of this wave (finished last iteration)
 #pragma unroll
           for (int h = 0; h < 4; ++h) xch[w][h][xw] = lg[h];
         }
-        *(DG_LDS u32x4*)(tile + wr + 512 * c) = e;
+        if (!(kC0Interleave && c == 0)) *(DG_LDS u32x4*)(tile + wr + 512 * c) = e;
         if (kDefer && c == 7 && defer) {
           // the late record of tile t-2, re-loaded in chunk 4: wait for it
           // here, then run the softmax steps skipped in chunks 4-6
@@ -950,10 +956,16 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           // e comes from memory, zf is constant: no VALU write precedes
-          if (c == 0)
+          if (c == 0) {
+            if constexpr (kC0Interleave) xch[w][h][xw] = lg[h];  // tile t-1's, row group h
             mfma16x32_v0(e, zf[h][c], lg[h]);  // a new tile's chain starts from 0
-          else
+            if constexpr (kC0Interleave) {
+              if (h == 3) *(DG_LDS u32x4*)(tile + wr) = e;
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
             mfma16x32_vn(e, zf[h][c], lg[h]);
+          }
           stage(c, h);
           if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
         }
